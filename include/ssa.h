@@ -1,0 +1,147 @@
+/*
+ * ssa.h -- C ABI of the MI355X (gfx950) spatial self-attention block.
+ *
+ * The operation (tensortonic problem "Spatial Self-Attention", diffusion
+ * L03: the formula, the prose under it and the parameter table):
+ *
+ *     Z   = tokens(GN(x))                     GN: num_groups groups, eps 1e-5,
+ *                                                 affine norm_weight/norm_bias
+ *     Q   = Z Wq^T + bq,  K = Z Wk^T + bk,  V = Z Wv^T + bv
+ *     O_j = softmax(Q_j K_j^T / sqrt(d)) V_j  head j = channels j*d..(j+1)*d-1,
+ *                                             d = C / num_heads, softmax over keys
+ *     out = x + image([O_1 .. O_n] Wo^T + bo)
+ *
+ * tokens() maps pixel (i, j) of each sample to token row i*W + j; image() is
+ * its inverse.  Weights are (C, C) stored (out, in) row-major, "as in a linear
+ * layer"; biases and the GroupNorm affine are (C,).
+ *
+ * Conventions for every entry point below
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers to contiguous row-major memory of
+ *   the element type `dtype` (x, out and all ten parameters share it):
+ *     x, out                          (B, C, H, W)   NCHW
+ *     norm_weight, norm_bias          (C,)
+ *     q_weight, k_weight, v_weight,
+ *     out_weight                      (C, C)         (out, in)
+ *     q_bias, k_bias, v_bias, out_bias (C,)
+ *   Every pointer must be 16-byte aligned.
+ * - The caller owns every buffer, including `workspace`.  The library
+ *   allocates no device memory and keeps no state between calls; calls on
+ *   different streams with different workspaces may run concurrently.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *   asynchronously; completion is observed through the stream.
+ * - Arguments are validated on the host before anything is enqueued.  On any
+ *   error nothing is launched and nothing is written.
+ * - B == 0, H == 0 or W == 0 is an empty input: SSA_OK, nothing launched, and
+ *   the data pointers may be NULL.
+ * - Supported: fp32 with 1 <= d <= 128; bf16 (fp32 accumulation) with
+ *   d in {32, 64, 96, 128}.  Other head sizes return SSA_E_UNSUPPORTED.
+ *
+ * Workspace (bytes from ssa_workspace_size; regions from
+ * ssa_get_workspace_layout, each 256-byte aligned):
+ *   gn_partial  float4 (count, mean, M2, 0) per (b, g, split)
+ *   gn_stats    float2 (mean, rstd) per (b, g)
+ *   gn_coef     float2 (a, s) per (b, c): GN(x)[b,c,t] = a*x[b,c,t] + s
+ *   q, k        (B, n, T, d)   dtype, token-major per head
+ *   vt          (B, n, d, Tp)  dtype, V transposed, Tp = T rounded up to 64;
+ *                              entries t >= T are never written
+ *   o           (B, T, C)      dtype, heads concatenated along channels
+ * After ssa_forward these hold the block's intermediates for inspection.
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSA_OK = 0,
+  SSA_E_NULL = 1,         /* a required pointer is NULL                         */
+  SSA_E_SHAPE = 2,        /* a size is negative, or C < 1                       */
+  SSA_E_CONSTRAINT = 3,   /* num_groups or num_heads < 1 or does not divide C   */
+  SSA_E_DTYPE = 4,        /* unknown dtype code                                 */
+  SSA_E_UNSUPPORTED = 5,  /* head size or total size outside the supported set  */
+  SSA_E_WORKSPACE = 6,    /* workspace_bytes < ssa_workspace_size(...)          */
+  SSA_E_ALIAS = 7,        /* out overlaps an input or the workspace, or the
+                             workspace overlaps an input                        */
+  SSA_E_ALIGN = 8,        /* a pointer is not 16-byte aligned                   */
+  SSA_E_HIP = 9,          /* a HIP launch failed (e.g. no gfx950 code object)   */
+  SSA_E_STAGE = 10        /* unknown stage code                                 */
+} ssa_status;
+
+typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+
+/* The four kernels of the block, in launch order. */
+typedef enum {
+  SSA_STAGE_GN_STATS = 0,   /* GroupNorm statistics -> gn_stats, gn_coef        */
+  SSA_STAGE_QKV = 1,        /* normalise + Q/K/V projections -> q, k, vt        */
+  SSA_STAGE_ATTENTION = 2,  /* per-head softmax(QK^T/sqrt(d))V -> o             */
+  SSA_STAGE_OUT_PROJ = 3    /* o Wo^T + bo + x, back to NCHW -> out             */
+} ssa_stage;
+
+typedef struct {
+  size_t total;        /* bytes, same as ssa_workspace_size                   */
+  size_t gn_partial;   /* byte offsets of each region from workspace start    */
+  size_t gn_stats;
+  size_t gn_coef;
+  size_t q;
+  size_t k;
+  size_t vt;
+  size_t o;
+  int64_t gn_splits;   /* splits per (b, g) segment in gn_partial             */
+  int64_t t_pad;       /* Tp: row pitch of vt in elements                     */
+} ssa_workspace_layout;
+
+/* Bytes of workspace ssa_forward needs for this problem, or 0 when the
+ * arguments would be rejected (see ssa_status) or the input is empty. */
+size_t ssa_workspace_size(int64_t B, int64_t C, int64_t H, int64_t W,
+                          int64_t num_groups, int64_t num_heads, int dtype);
+
+/* Fills *layout with the workspace regions for this problem.
+ * Returns SSA_E_NULL when layout is NULL, else the status ssa_forward would
+ * return for these sizes before looking at pointers. */
+ssa_status ssa_get_workspace_layout(int64_t B, int64_t C, int64_t H, int64_t W,
+                                    int64_t num_groups, int64_t num_heads, int dtype,
+                                    ssa_workspace_layout* layout);
+
+/* The whole block: enqueues the four stages on `stream`.
+ * Parameter order follows the problem's parameter table. */
+ssa_status ssa_forward(const void* x, void* out,
+                       const void* norm_weight, const void* norm_bias,
+                       const void* q_weight, const void* k_weight,
+                       const void* v_weight, const void* out_weight,
+                       const void* q_bias, const void* k_bias,
+                       const void* v_bias, const void* out_bias,
+                       int64_t B, int64_t C, int64_t H, int64_t W,
+                       int64_t num_groups, int64_t num_heads, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* One stage of the block, with the same arguments and validation as
+ * ssa_forward.  Running stages 0, 1, 2, 3 in order on one stream with one
+ * workspace is exactly ssa_forward.  A stage reads what the earlier stages
+ * left in the workspace; running it out of order computes from whatever the
+ * workspace holds (no error is detectable).  Used to time and inspect each
+ * kernel separately. */
+ssa_status ssa_forward_stage(int stage,
+                             const void* x, void* out,
+                             const void* norm_weight, const void* norm_bias,
+                             const void* q_weight, const void* k_weight,
+                             const void* v_weight, const void* out_weight,
+                             const void* q_bias, const void* k_bias,
+                             const void* v_bias, const void* out_bias,
+                             int64_t B, int64_t C, int64_t H, int64_t W,
+                             int64_t num_groups, int64_t num_heads, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ssa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

@@ -1,0 +1,92 @@
+"""MI355X (gfx950) spatial self-attention block.
+
+    out = x + image(MHA(tokens(GN(x))))
+
+(tensortonic problem "Spatial Self-Attention": GroupNorm, pixel tokens, Q/K/V
+projections with biases, per-head softmax(Q_j K_j^T / sqrt(d)) V_j,
+concatenated heads, output projection, residual in image layout.)
+
+The computation runs in libssa.so's HIP kernels behind the C ABI in
+include/ssa.h; this module only moves pointers.  torch supplies device memory
+and the current stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, PARAM_ORDER, SSA_BF16, SSA_F32, STAGES, SSAError, SSAValueError,
+    lib, ssa_forward, ssa_forward_stage, ssa_get_workspace_layout, ssa_status_string,
+    ssa_workspace_size,
+)
+from ._binding import _raise
+
+_DTYPES = {torch.float32: SSA_F32, torch.bfloat16: SSA_BF16}
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise SSAValueError(4, f"dtype {dtype}")
+    return _DTYPES[dtype]
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr() if t.numel() else 0
+
+
+def _check_tensors(x: torch.Tensor, params: dict):
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor (the block runs only in the HIP kernels)")
+    if x.dim() != 4:
+        raise ValueError("x must be (B, C, H, W)")
+    if set(params) != set(PARAM_ORDER):
+        raise ValueError(f"params must have exactly the keys {PARAM_ORDER}")
+    C = x.shape[1]
+    for k in PARAM_ORDER:
+        p = params[k]
+        want = (C,) if (k.endswith("_bias") or k.startswith("norm")) else (C, C)
+        if tuple(p.shape) != want:
+            raise ValueError(f"{k} must have shape {want}, got {tuple(p.shape)}")
+        if p.dtype != x.dtype or p.device != x.device:
+            raise ValueError(f"{k} must match x's dtype and device")
+        if not p.is_contiguous():
+            raise ValueError(f"{k} must be contiguous")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (NCHW)")
+
+
+def workspace_for(x: torch.Tensor, num_groups: int, num_heads: int) -> torch.Tensor:
+    """A workspace tensor (uint8) of ssa_workspace_size bytes on x's device."""
+    B, C, H, W = x.shape
+    n = ssa_workspace_size(B, C, H, W, num_groups, num_heads, dtype_code(x.dtype))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+
+
+def forward_into(x, params, num_groups, num_heads, out, workspace, stage=None,
+                 stream=None) -> None:
+    """Enqueue the block (or one stage of it) on `stream` (default: torch's current)."""
+    _check_tensors(x, params)
+    B, C, H, W = x.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    ptrs = [_ptr(params[k]) for k in PARAM_ORDER]
+    args = (_ptr(x), _ptr(out), ptrs, B, C, H, W, num_groups, num_heads, dtype_code(x.dtype),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if stage is None:
+        _raise(ssa_forward(*args), "ssa_forward")
+    else:
+        _raise(ssa_forward_stage(STAGES.get(stage, stage), *args), "ssa_forward_stage")
+
+
+def spatial_self_attention(x: torch.Tensor, params: dict, num_groups: int,
+                           num_heads: int) -> torch.Tensor:
+    """out = x + image(MHA(tokens(GN(x)))), shape and dtype of x.
+
+    params holds the ten tensors norm_weight, norm_bias (C,), q/k/v/out_weight
+    (C, C) stored (out, in), q/k/v/out_bias (C,), all of x's dtype.
+    """
+    _check_tensors(x, params)
+    out = torch.empty_like(x)
+    ws = workspace_for(x, num_groups, num_heads)
+    forward_into(x, params, num_groups, num_heads, out, ws)
+    return out

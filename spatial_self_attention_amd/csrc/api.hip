@@ -1,0 +1,208 @@
+// Host side of the C ABI declared in include/ssa.h: argument validation,
+// launch planning, workspace layout and stage dispatch.  Nothing here touches
+// device memory; every check runs before the first launch.
+#include <string.h>
+
+#include "ssa_internal.h"
+
+namespace ssa {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;  // per tensor, for 32-bit row math
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool supported_head(int dtype, int64_t d) {
+  if (dtype == SSA_F32) return d >= 1 && d <= 128;
+  return d == 32 || d == 64 || d == 96 || d == 128;
+}
+
+// Size checks shared by every entry point.  On success fills *p (when the
+// input is non-empty) and sets *empty.
+ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
+                     int64_t n, int dtype, Plan* p, bool* empty) {
+  if (dtype != SSA_F32 && dtype != SSA_BF16) return SSA_E_DTYPE;
+  if (B < 0 || H < 0 || W < 0 || C < 1) return SSA_E_SHAPE;
+  if (G < 1 || n < 1 || C % G != 0 || C % n != 0) return SSA_E_CONSTRAINT;
+  const int64_t d = C / n;
+  if (!supported_head(dtype, d)) return SSA_E_UNSUPPORTED;
+  *empty = (B == 0 || H == 0 || W == 0);
+  if (*empty) return SSA_OK;
+  const int64_t T = H * W;
+  if (T > kMaxElems || B > kMaxElems / T || B * T > kMaxElems / (3 * C))
+    return SSA_E_UNSUPPORTED;
+  memset(p, 0, sizeof(*p));
+  p->B = B; p->C = C; p->H = H; p->W = W; p->G = G; p->n = n;
+  p->T = T; p->d = d;
+  p->Tp = (T + kTokPad - 1) / kTokPad * kTokPad;
+  p->dtype = dtype;
+  p->esize = dtype == SSA_F32 ? 4 : 2;
+
+  // Statistics split: aim for about 2048 work-groups over the whole input,
+  // with at least 2048 elements per work-group.
+  const int64_t L = (C / G) * T;
+  const int vec = 16 / p->esize;
+  p->gn_vec = (L % vec == 0) ? vec : 1;
+  p->seg_len = L;
+  int64_t segs = B * G;
+  int64_t want = (2048 + segs - 1) / segs;
+  int64_t cap = (L + 2047) / 2048;
+  int64_t splits = want < cap ? want : cap;
+  if (splits < 1) splits = 1;
+  int64_t chunk = (L + splits - 1) / splits;
+  chunk = (chunk + p->gn_vec - 1) / p->gn_vec * p->gn_vec;
+  p->chunk = chunk;
+  p->splits = (L + chunk - 1) / chunk;
+
+  ssa_workspace_layout& ws = p->ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kAlign); return o; };
+  ws.gn_partial = take(size_t(segs * p->splits) * 16);
+  ws.gn_stats = take(size_t(segs) * 8);
+  ws.gn_coef = take(size_t(B * C) * 8);
+  const size_t e = p->esize;
+  ws.q = take(size_t(B * n * T * d) * e);
+  ws.k = take(size_t(B * n * T * d) * e);
+  ws.vt = take(size_t(B * n * d * p->Tp) * e);
+  ws.o = take(size_t(B * T * C) * e);
+  ws.total = off;
+  ws.gn_splits = p->splits;
+  ws.t_pad = p->Tp;
+  return SSA_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+ssa_status check_pointers(const Plan& p, const Args& a, size_t ws_bytes) {
+  const void* ptrs[] = {a.x, a.out, a.norm_weight, a.norm_bias, a.w[0], a.w[1], a.w[2], a.w[3],
+                        a.b[0], a.b[1], a.b[2], a.b[3], a.ws};
+  for (const void* q : ptrs)
+    if (q == nullptr) return SSA_E_NULL;
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return SSA_E_ALIGN;
+  if (ws_bytes < p.ws.total) return SSA_E_WORKSPACE;
+  const size_t e = p.esize;
+  const size_t img = size_t(p.B * p.C * p.T) * e;
+  auto rng = [](const void* q, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+    return Range{lo, lo + bytes};
+  };
+  Range out = rng(a.out, img);
+  Range ws = rng(a.ws, p.ws.total);
+  Range inputs[] = {rng(a.x, img),
+                    rng(a.norm_weight, p.C * e), rng(a.norm_bias, p.C * e),
+                    rng(a.w[0], p.C * p.C * e), rng(a.w[1], p.C * p.C * e),
+                    rng(a.w[2], p.C * p.C * e), rng(a.w[3], p.C * p.C * e),
+                    rng(a.b[0], p.C * e), rng(a.b[1], p.C * e),
+                    rng(a.b[2], p.C * e), rng(a.b[3], p.C * e)};
+  if (overlap(out, ws)) return SSA_E_ALIAS;
+  for (const Range& r : inputs)
+    if (overlap(out, r) || overlap(ws, r)) return SSA_E_ALIAS;
+  return SSA_OK;
+}
+
+ssa_status run(int first, int last, const void* x, void* out, const void* nw, const void* nb,
+               const void* qw, const void* kw, const void* vw, const void* ow,
+               const void* qb, const void* kb, const void* vb, const void* ob,
+               int64_t B, int64_t C, int64_t H, int64_t W, int64_t G, int64_t n, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  bool empty = false;
+  ssa_status st = make_plan(B, C, H, W, G, n, dtype, &p, &empty);
+  if (st != SSA_OK || empty) return st;
+  Args a;
+  a.x = x; a.out = out; a.norm_weight = nw; a.norm_bias = nb;
+  a.w[0] = qw; a.w[1] = kw; a.w[2] = vw; a.w[3] = ow;
+  a.b[0] = qb; a.b[1] = kb; a.b[2] = vb; a.b[3] = ob;
+  a.ws = static_cast<char*>(workspace);
+  a.stream = static_cast<hipStream_t>(stream);
+  st = check_pointers(p, a, workspace_bytes);
+  if (st != SSA_OK) return st;
+  for (int s = first; s <= last; ++s) {
+    hipError_t e = hipSuccess;
+    switch (s) {
+      case SSA_STAGE_GN_STATS: e = launch_gn_stats(p, a); break;
+      case SSA_STAGE_QKV: e = launch_qkv_proj(p, a); break;
+      case SSA_STAGE_ATTENTION: e = launch_attention(p, a); break;
+      case SSA_STAGE_OUT_PROJ: e = launch_out_proj(p, a); break;
+    }
+    if (e != hipSuccess) return SSA_E_HIP;
+  }
+  return SSA_OK;
+}
+
+}  // namespace
+}  // namespace ssa
+
+extern "C" {
+
+size_t ssa_workspace_size(int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
+                          int64_t num_heads, int dtype) {
+  ssa::Plan p;
+  bool empty = false;
+  if (ssa::make_plan(B, C, H, W, num_groups, num_heads, dtype, &p, &empty) != SSA_OK || empty)
+    return 0;
+  return p.ws.total;
+}
+
+ssa_status ssa_get_workspace_layout(int64_t B, int64_t C, int64_t H, int64_t W,
+                                    int64_t num_groups, int64_t num_heads, int dtype,
+                                    ssa_workspace_layout* layout) {
+  if (layout == nullptr) return SSA_E_NULL;
+  ssa::Plan p;
+  bool empty = false;
+  ssa_status st = ssa::make_plan(B, C, H, W, num_groups, num_heads, dtype, &p, &empty);
+  memset(layout, 0, sizeof(*layout));
+  if (st == SSA_OK && !empty) *layout = p.ws;
+  return st;
+}
+
+ssa_status ssa_forward(const void* x, void* out, const void* norm_weight, const void* norm_bias,
+                       const void* q_weight, const void* k_weight, const void* v_weight,
+                       const void* out_weight, const void* q_bias, const void* k_bias,
+                       const void* v_bias, const void* out_bias, int64_t B, int64_t C, int64_t H,
+                       int64_t W, int64_t num_groups, int64_t num_heads, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return ssa::run(SSA_STAGE_GN_STATS, SSA_STAGE_OUT_PROJ, x, out, norm_weight, norm_bias,
+                  q_weight, k_weight, v_weight, out_weight, q_bias, k_bias, v_bias, out_bias,
+                  B, C, H, W, num_groups, num_heads, dtype, workspace, workspace_bytes, stream);
+}
+
+ssa_status ssa_forward_stage(int stage, const void* x, void* out, const void* norm_weight,
+                             const void* norm_bias, const void* q_weight, const void* k_weight,
+                             const void* v_weight, const void* out_weight, const void* q_bias,
+                             const void* k_bias, const void* v_bias, const void* out_bias,
+                             int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
+                             int64_t num_heads, int dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (stage < SSA_STAGE_GN_STATS || stage > SSA_STAGE_OUT_PROJ) return SSA_E_STAGE;
+  return ssa::run(stage, stage, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight,
+                  out_weight, q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups,
+                  num_heads, dtype, workspace, workspace_bytes, stream);
+}
+
+const char* ssa_status_string(int status) {
+  switch (status) {
+    case SSA_OK: return "ok";
+    case SSA_E_NULL: return "a required pointer is NULL";
+    case SSA_E_SHAPE: return "invalid shape: sizes must be >= 0 and C >= 1";
+    case SSA_E_CONSTRAINT: return "num_groups and num_heads must be >= 1 and divide C";
+    case SSA_E_DTYPE: return "unknown dtype";
+    case SSA_E_UNSUPPORTED:
+      return "unsupported size: head size must be 1..128 (fp32) or 32/64/96/128 (bf16), "
+             "and each tensor below 2^31 elements";
+    case SSA_E_WORKSPACE: return "workspace smaller than ssa_workspace_size()";
+    case SSA_E_ALIAS: return "out or workspace overlaps another buffer";
+    case SSA_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case SSA_E_HIP: return "a HIP kernel launch failed";
+    case SSA_E_STAGE: return "unknown stage";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

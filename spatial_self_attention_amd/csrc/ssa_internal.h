@@ -1,0 +1,63 @@
+// Internal declarations shared by the HIP sources of libssa (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssa.h"
+
+namespace ssa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kGnEps = 1e-5f;
+constexpr int kTokPad = 64;  // vt row pitch is T rounded up to this
+
+// Everything a launch needs, derived once from the sizes by make_plan().
+struct Plan {
+  int64_t B, C, H, W, G, n;
+  int64_t T, d, Tp;
+  int dtype;       // ssa_dtype
+  int esize;       // bytes per element of x / params / q,k,vt,o
+  // GroupNorm statistics split: each (b, g) segment of Cg*T contiguous
+  // elements is cut into `splits` chunks of `chunk` elements.
+  int64_t seg_len, chunk, splits;
+  int gn_vec;      // elements per vector load in the stats pass (1 = scalar)
+  ssa_workspace_layout ws;
+};
+
+// Pointers of one call, already validated.
+struct Args {
+  const void* x;
+  void* out;
+  const void* norm_weight;
+  const void* norm_bias;
+  const void* w[4];  // q, k, v, out weights
+  const void* b[4];  // q, k, v, out biases
+  char* ws;
+  hipStream_t stream;
+};
+
+// Launchers (one per stage); each returns hipSuccess or the launch error.
+hipError_t launch_gn_stats(const Plan& p, const Args& a);
+hipError_t launch_qkv_proj(const Plan& p, const Args& a);
+hipError_t launch_attention(const Plan& p, const Args& a);
+hipError_t launch_out_proj(const Plan& p, const Args& a);
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+}  // namespace ssa

@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+include/ssa.h declares, sizes its workspace, and rejects bad arguments on the
+host before anything is launched.
+
+Pointers passed here are fake (never dereferenced): every case returns an
+error status from host-side validation, or is an empty input that launches
+nothing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import spatial_self_attention_amd as ssa
+from spatial_self_attention_amd import _binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+S = {name: code for code, name in bnd.STATUS_NAMES.items()}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ssa.lib()
+    names = declared_functions()
+    assert set(names) == set(bnd.EXPORTS), names
+    for name in names:
+        assert hasattr(L, name), f"libssa.so does not export {name}"
+
+
+def test_status_strings():
+    for code in list(bnd.STATUS_NAMES) + [99, -1]:
+        s = ssa.ssa_status_string(code)
+        assert isinstance(s, str) and s
+    assert ssa.ssa_status_string(0) == "ok"
+
+
+def _layout_expect(B, C, H, W, G, n, esize):
+    T = H * W
+    d = C // n
+    Tp = (T + 63) // 64 * 64
+    return {
+        "gn_stats": B * G * 8, "gn_coef": B * C * 8,
+        "q": B * n * T * d * esize, "k": B * n * T * d * esize,
+        "vt": B * n * d * Tp * esize, "o": B * T * C * esize,
+    }
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 64, 8, 8, 8, 2, ssa.SSA_F32),
+    (64, 512, 14, 14, 32, 4, ssa.SSA_BF16),
+    (16, 512, 16, 16, 32, 8, ssa.SSA_BF16),
+    (4, 320, 64, 64, 32, 5, ssa.SSA_BF16),
+    (2, 640, 96, 96, 32, 10, ssa.SSA_BF16),
+    (2, 4, 1, 1, 4, 2, ssa.SSA_F32),
+    (1, 2, 2, 3, 1, 1, ssa.SSA_F32),
+])
+def test_workspace_layout(shape):
+    B, C, H, W, G, n, dt = shape
+    lay = ssa.ssa_get_workspace_layout(B, C, H, W, G, n, dt)
+    assert lay["total"] == ssa.ssa_workspace_size(B, C, H, W, G, n, dt)
+    esize = 4 if dt == ssa.SSA_F32 else 2
+    want = _layout_expect(B, C, H, W, G, n, esize)
+    want["gn_partial"] = B * G * lay["gn_splits"] * 16
+    order = ["gn_partial", "gn_stats", "gn_coef", "q", "k", "vt", "o"]
+    for a, b in zip(order, order[1:]):
+        assert lay[a] % 256 == 0
+        assert lay[a] + want[a] <= lay[b], (a, b)
+    assert lay["o"] + want["o"] <= lay["total"]
+    assert lay["t_pad"] % 64 == 0 and lay["t_pad"] >= H * W
+    assert lay["gn_splits"] >= 1
+    # every chunk of a segment is non-empty
+    L = (C // G) * H * W
+    assert (lay["gn_splits"] - 1) * -(-L // lay["gn_splits"]) < L
+
+
+def test_workspace_size_zero_when_rejected_or_empty():
+    assert ssa.ssa_workspace_size(1, 6, 2, 2, 4, 2, ssa.SSA_F32) == 0     # 4 does not divide 6
+    assert ssa.ssa_workspace_size(1, 64, 2, 2, 8, 4, ssa.SSA_BF16) == 0   # d = 16 in bf16
+    assert ssa.ssa_workspace_size(0, 64, 8, 8, 8, 2, ssa.SSA_F32) == 0    # empty
+    assert ssa.ssa_workspace_size(1, 64, 8, 8, 8, 2, 5) == 0              # dtype
+
+
+class Fake:
+    """Distinct, 256-byte aligned fake device addresses, far apart."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes=1 << 30):
+        p = self.next
+        self.next += (nbytes + (1 << 20)) // 256 * 256 + 256
+        return p
+
+
+def call(status_fn="ssa_forward", stage=None, **kw):
+    B, C, H, W, G, n, dt = kw["shape"]
+    fake = Fake()
+    ptr = {k: fake() for k in ["x", "out", "ws"] + list(bnd.PARAM_ORDER)}
+    ptr.update(kw.get("ptr", {}))
+    ws_bytes = kw.get("ws_bytes", ssa.ssa_workspace_size(B, C, H, W, G, n, dt) or 1 << 20)
+    params = [ptr[k] for k in bnd.PARAM_ORDER]
+    if status_fn == "ssa_forward":
+        return ssa.ssa_forward(ptr["x"], ptr["out"], params, B, C, H, W, G, n, dt,
+                               ptr["ws"], ws_bytes, 0)
+    return ssa.ssa_forward_stage(stage, ptr["x"], ptr["out"], params, B, C, H, W, G, n, dt,
+                                 ptr["ws"], ws_bytes, 0)
+
+
+OK_SHAPE = (2, 64, 4, 4, 8, 2, ssa.SSA_BF16)
+
+
+@pytest.mark.parametrize("case,kw,want", [
+    ("bad dtype", dict(shape=(2, 64, 4, 4, 8, 2, 3)), "SSA_E_DTYPE"),
+    ("C = 0", dict(shape=(2, 0, 4, 4, 1, 1, ssa.SSA_F32)), "SSA_E_SHAPE"),
+    ("negative B", dict(shape=(-1, 64, 4, 4, 8, 2, ssa.SSA_F32)), "SSA_E_SHAPE"),
+    ("negative H", dict(shape=(1, 64, -4, 4, 8, 2, ssa.SSA_F32)), "SSA_E_SHAPE"),
+    ("G does not divide C", dict(shape=(2, 64, 4, 4, 7, 2, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
+    ("n does not divide C", dict(shape=(2, 64, 4, 4, 8, 3, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
+    ("G = 0", dict(shape=(2, 64, 4, 4, 0, 2, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
+    ("n = 0", dict(shape=(2, 64, 4, 4, 8, 0, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
+    ("bf16 d = 16", dict(shape=(2, 64, 4, 4, 8, 4, ssa.SSA_BF16)), "SSA_E_UNSUPPORTED"),
+    ("bf16 d = 48", dict(shape=(2, 96, 4, 4, 8, 2, ssa.SSA_BF16)), "SSA_E_UNSUPPORTED"),
+    ("fp32 d = 256", dict(shape=(2, 256, 4, 4, 8, 1, ssa.SSA_F32)), "SSA_E_UNSUPPORTED"),
+    ("too many elements", dict(shape=(1 << 20, 512, 64, 64, 32, 4, ssa.SSA_BF16)),
+     "SSA_E_UNSUPPORTED"),
+    ("null x", dict(shape=OK_SHAPE, ptr={"x": 0}), "SSA_E_NULL"),
+    ("null out", dict(shape=OK_SHAPE, ptr={"out": 0}), "SSA_E_NULL"),
+    ("null v_bias", dict(shape=OK_SHAPE, ptr={"v_bias": 0}), "SSA_E_NULL"),
+    ("null workspace", dict(shape=OK_SHAPE, ptr={"ws": 0}), "SSA_E_NULL"),
+    ("misaligned x", dict(shape=OK_SHAPE, ptr={"x": (1 << 50) + 8}), "SSA_E_ALIGN"),
+    ("misaligned weight", dict(shape=OK_SHAPE, ptr={"k_weight": (1 << 50) + 2}), "SSA_E_ALIGN"),
+    ("workspace too small", dict(shape=OK_SHAPE, ws_bytes=1024), "SSA_E_WORKSPACE"),
+    ("out is x", dict(shape=OK_SHAPE, ptr={"x": 1 << 50, "out": 1 << 50}), "SSA_E_ALIAS"),
+    ("out overlaps x", dict(shape=OK_SHAPE, ptr={"x": 1 << 50, "out": (1 << 50) + 256}),
+     "SSA_E_ALIAS"),
+    ("out overlaps a weight", dict(shape=OK_SHAPE, ptr={"out_weight": 1 << 50,
+                                                        "out": (1 << 50) + 4096}), "SSA_E_ALIAS"),
+    ("workspace overlaps a bias", dict(shape=OK_SHAPE, ptr={"ws": 1 << 50,
+                                                            "q_bias": (1 << 50) + 512}),
+     "SSA_E_ALIAS"),
+    ("workspace overlaps out", dict(shape=OK_SHAPE, ptr={"ws": 1 << 50, "out": (1 << 50) + 512}),
+     "SSA_E_ALIAS"),
+])
+def test_rejections(case, kw, want):
+    assert bnd.STATUS_NAMES[call(**kw)] == want, case
+    assert bnd.STATUS_NAMES[call("stage", stage=2, **kw)] == want, case
+
+
+def test_unknown_stage():
+    assert bnd.STATUS_NAMES[call("stage", stage=4, shape=OK_SHAPE)] == "SSA_E_STAGE"
+    assert bnd.STATUS_NAMES[call("stage", stage=-1, shape=OK_SHAPE)] == "SSA_E_STAGE"
+
+
+@pytest.mark.parametrize("shape", [(0, 64, 8, 8, 8, 2, ssa.SSA_BF16),
+                                   (2, 64, 0, 8, 8, 2, ssa.SSA_F32),
+                                   (2, 64, 8, 0, 8, 2, ssa.SSA_F32)])
+def test_empty_input_is_a_no_op(shape):
+    B, C, H, W, G, n, dt = shape
+    params = [0] * 10
+    st = ssa.ssa_forward(0, 0, params, B, C, H, W, G, n, dt, 0, 0, 0)
+    assert st == 0
+
+
+def test_layout_null_pointer():
+    L = ssa.lib()
+    assert L.ssa_get_workspace_layout(1, 64, 8, 8, 8, 2, 0, None) == S["SSA_E_NULL"]
+
+
+def test_python_wrapper_rejects_cpu_tensor():
+    import torch
+    x = torch.zeros(1, 4, 2, 2)
+    p = {k: torch.zeros((4, 4) if k.endswith("weight") and not k.startswith("norm") else (4,))
+         for k in bnd.PARAM_ORDER}
+    with pytest.raises(ValueError):
+        ssa.spatial_self_attention(x, p, 2, 2)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bnd, "_lib", None)
+    monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "libssa.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bnd.lib()
