@@ -1,0 +1,240 @@
+"""Throughput of the spatial self-attention block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I] [--no-cpu]
+
+A step is one ssa_forward over one batch of the selected workload (GroupNorm
+statistics, QKV projection, flash attention, output projection + residual),
+with inputs already resident in HBM.  W untimed steps, then exactly K steps
+between two device synchronisations; the value is block TFLOP/s
+(8BTC^2 + 4BT^2C flops per step).  Prints one JSON line.
+
+Also reported:
+* per-kernel average durations from HIP events on the launch stream, each
+  stage replayed back-to-back from a HIP graph so host launch overhead is not
+  counted; the dominant kernel's roofline (algorithmic flops or bytes per
+  launch over its average duration, against MI355X's dense bf16 MFMA peak or
+  HBM bandwidth), with HBM traffic from the stored rocprofv3 counter summary
+  when it was taken on the current kernel sources;
+* the fp64 CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+DEFAULT_CONFIG = 1          # BoTNet-c5: B64 C512 14x14 G32 n4 (d=128), bf16
+
+
+def source_digest() -> str:
+    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "spatial_self_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stage_work(wl):
+    """Algorithmic work per launch of each stage: (kind, amount)."""
+    B, C, T = wl.B, wl.C, wl.T
+    es = 4 if wl.dtype == "f32" else 2
+    return {
+        "gn_stats": ("bytes", B * C * T * es),
+        "qkv": ("flops", 6 * B * T * C * C),
+        "attention": ("flops", 4 * B * T * T * C),
+        "out_proj": ("flops", 2 * B * T * C * C),
+    }
+
+
+# Kernel names (as rocprofv3 prints them) behind each stage, for the counters.
+STAGE_KERNELS = {
+    "gn_stats": "gn_partial_kernel",
+    "qkv": "proj_bf16_kernel<0",
+    "attention": "attn_bf16_kernel",
+    "out_proj": "proj_bf16_kernel<1",
+}
+
+
+def stored_traffic(stage: str, wl_name: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    if data.get("source_digest") != source_digest():
+        return None
+    ent = data.get("entries", {}).get(f"{wl_name}|{stage}")
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, seed, budget_s=12.0):
+    """The fp64 oracle as it is, on a bounded sample: whole samples of the batch."""
+    from oracle import forward as oracle_forward
+    from spatial_self_attention_amd.inputs import draw, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    one = wl.replace(B=1)
+    done, flops, el = 0, 0, 0.0
+    while done < wl.B and el < budget_s:
+        x64, p64 = to_f64(*draw(one, seed + done))
+        t1 = time.perf_counter()
+        oracle_forward(x64, p64, wl.num_groups, wl.num_heads)
+        el += time.perf_counter() - t1
+        done += 1
+        flops += one.flops()
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {wl.B} samples of {wl.name}, one whole sample per oracle "
+                      f"call, fp64 NumPy, {el:.1f} s of oracle time",
+            "pixels_per_s": done * wl.T / el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="time K steps replayed from one HIP graph instead of eager launches")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the block runs on a single MI355X here; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import spatial_self_attention_amd as ssa
+    from spatial_self_attention_amd.inputs import WORKLOADS, default_seed, draw
+
+    wl = WORKLOADS[args.config]
+    seed = default_seed(args.config)
+    dev = torch.device("cuda:0")
+    x, p = draw(wl, seed)
+    xg = x.to(dev)
+    pg = {k: v.to(dev) for k, v in p.items()}
+    out = torch.empty_like(xg)
+    ws = ssa.workspace_for(xg, wl.num_groups, wl.num_heads)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():  # on torch's current stream (the capture stream inside a graph)
+        ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if args.graph:
+        g.replay()
+    else:
+        for _ in range(args.steps):
+            step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = e0.elapsed_time(e1) / 1e3
+    elapsed = max(wall, gpu_s)
+    ms_per_step = elapsed / args.steps * 1e3
+    tflops = wl.flops() * args.steps / elapsed / 1e12
+
+    # ---- per-kernel durations: each stage replayed back-to-back from a graph ----
+    reps = max(20, min(args.steps, 200))
+    per_stage = {}
+    for stage in ("gn_stats", "qkv", "attention", "out_proj"):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws, stage=stage)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_stage[stage] = a.elapsed_time(b) / 1e3 / reps
+        del g
+    # restore a full, consistent result in `out`
+    step()
+    torch.cuda.synchronize()
+
+    work = stage_work(wl)
+    dom = max(("qkv", "attention", "out_proj"), key=lambda s: per_stage[s])
+    kind, amount = work[dom]
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = amount / per_stage[dom] / 1e12
+    traffic = stored_traffic(dom, wl.name)
+    roofline = {"bound": "mfma", "kernel": STAGE_KERNELS[dom], "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic, "avg_launch_us": round(per_stage[dom] * 1e6, 2),
+                "algorithmic_per_launch": amount}
+    gn_bytes = work["gn_stats"][1]
+    kernels = {s: {"avg_us": round(t * 1e6, 2),
+                   ("TFLOP/s" if work[s][0] == "flops" else "GB/s"):
+                       round(work[s][1] / t / (1e12 if work[s][0] == "flops" else 1e9), 2)}
+               for s, t in per_stage.items()}
+
+    line = {
+        "metric": "block TFLOP/s",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded, workload distributions)",
+        "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
+                   "num_groups": wl.num_groups, "num_heads": wl.num_heads, "d": wl.d,
+                   "launch": "graph" if args.graph else "eager"},
+        "pixels_per_s": round(wl.B * wl.T / elapsed * args.steps, 1),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "gn_stats_GBps": round(gn_bytes / per_stage["gn_stats"] / 1e9, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, seed)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
