@@ -22,10 +22,12 @@ LIB = os.path.join(PKG, "libssa.so")
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled: the compiler still vectorises plain
-# float code, but without the v_pk_*_f32 forms.
+# float code, but without the v_pk_*_f32 forms.  MFMA accumulators are kept in
+# ordinary VGPRs (no AGPR copies around the softmax and epilogues).
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -10,9 +10,11 @@
 //
 // with the scores in the log2 domain (s = q.k * log2(e) / sqrt(d)).
 //
-// bf16 kernel (gfx950 MFMA): 4 waves x 32 queries, key tiles of 64.  The
-// score block is formed TRANSPOSED, S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
-// so each lane holds one query (its column) and 16 keys per 32-key block:
+// bf16 kernel (gfx950 MFMA): 4 waves x 32 queries per work-group, key tiles of
+// 64 double-buffered in LDS (the next tile is fetched into registers while the
+// current one is used).  The score block is formed TRANSPOSED, S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16, so each lane holds one query (its column) and 16
+// keys per 32-key sub-block:
 //  * the row max / row sum need no shuffles except one exchange with lane^32
 //    (the other half of the keys of the same query);
 //  * the rescale by 2^(m - m') is per lane;
@@ -22,6 +24,10 @@
 //    not depend on the order of its terms).
 // V is read from the transposed (d, Tp) layout, so each V^T operand is two
 // 8-byte LDS reads.  O is written token-major (B, T, C), heads concatenated.
+// The softmax runs per 32-key sub-block; the QK^T MFMAs of the next sub-block
+// are issued before it so matrix-core and VALU work overlap.  O and l are
+// rescaled lazily: only when a row max grows by more than 2^8.  Row sums are
+// taken with v_dot2 over the same bf16-rounded probabilities that enter P V.
 //
 // fp32 kernel: 64 queries x 4 lanes per query (each lane owns d/4 dims),
 // FMA only, key tiles of 32 in LDS.
@@ -47,21 +53,213 @@ struct AttnParams {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-constexpr int QT = 128;  // queries per work-group
-constexpr int KT = 64;   // keys per tile
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
+constexpr float kLazyLog2 = 8.f;  // rescale O only when the row max grows by more than 2^8
+
+// Work-group id -> logical id so that consecutive logical ids (query tiles of
+// one head, which share K and V) run on the same XCD: work-groups are handed
+// to the 8 XCDs round-robin, so XCD x receives ids x, x+8, x+16, ...
+__device__ __forceinline__ int xcd_remap(int w, int nwg) {
+  const int q = nwg >> 3, r = nwg & 7, x = w & 7;
+  return x * q + min(x, r) + (w >> 3);
+}
+
+template <int D, int QB, int KT>
+struct Tile {
+  static constexpr int QPW = 32 * QB;      // queries per wave
+  static constexpr int QT = 4 * QPW;       // queries per work-group (4 waves)
+  static constexpr int NKB = KT / 32;      // 32-key sub-blocks per tile
+  static constexpr int KP = D + 8;         // K tile row pitch (bf16)
+  static constexpr int VP = KT + 8;        // V^T tile row pitch (bf16)
+  static constexpr int KSZ = KT * KP;      // K tile (bf16 elements)
+  static constexpr int VSZ = D * VP;       // V^T tile
+  static constexpr int BUF = KSZ + VSZ;
+  static constexpr int VPT = KT * D / 8 / 256;  // 16-byte vectors per thread per operand
+};
+
+template <int D, int QB>
+struct AttnState {
+  bf16x8 qf[QB][D / 16];   // B operand of S^T = K Q^T, one query per lane column
+  f32x16 o[QB][D / 32];    // O^T accumulators (d x 32 queries per block)
+  float m[QB];             // running row max, raw score units
+  float l[QB];             // running row sum (this lane's half of the keys)
+};
+
+// Registers holding the next K and V^T tiles while the current one is used.
+template <int D, int QB, int KT>
+struct Prefetch {
+  bf16x8 k[Tile<D, QB, KT>::VPT];
+  bf16x8 v[Tile<D, QB, KT>::VPT];
+};
+
+// Global -> registers for one K tile and one V^T tile (keys k0 .. k0+KT-1).
+// MASK: keys >= T read as zero (K rows are clamped to stay inside the head).
+template <int D, int QB, int KT, bool MASK>
+__device__ __forceinline__ void load_tile(Prefetch<D, QB, KT>& pf, const bf16* K, const bf16* Vt,
+                                          int Tp, int k0, int T, int tid) {
+  const bf16x8 zero8 = {};
+#pragma unroll
+  for (int i = 0; i < Tile<D, QB, KT>::VPT; ++i) {
+    const int v = tid + 256 * i;
+    const int r = v / (D / 8), c8 = v % (D / 8);
+    const int key = k0 + r;
+    if (MASK) {
+      const bf16x8 val =
+          *reinterpret_cast<const bf16x8*>(K + int64_t(min(key, T - 1)) * D + c8 * 8);
+      pf.k[i] = key < T ? val : zero8;
+    } else {
+      pf.k[i] = *reinterpret_cast<const bf16x8*>(K + int64_t(key) * D + c8 * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Tile<D, QB, KT>::VPT; ++i) {
+    const int v = tid + 256 * i;
+    const int r = v / (KT / 8), c8 = v % (KT / 8);
+    const int key = k0 + c8 * 8;
+    // rows have Tp >= k0 + KT entries, so the vector read stays in the row
+    bf16x8 val = *reinterpret_cast<const bf16x8*>(Vt + int64_t(r) * Tp + key);
+    if (MASK) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key + e >= T) val[e] = static_cast<bf16>(0.f);
+    }
+    pf.v[i] = val;
+  }
+}
+
+template <int D, int QB, int KT>
+__device__ __forceinline__ void store_tile(bf16* buf, const Prefetch<D, QB, KT>& pf, int tid) {
+  typedef Tile<D, QB, KT> TL;
+#pragma unroll
+  for (int i = 0; i < TL::VPT; ++i) {
+    const int v = tid + 256 * i;
+    const int r = v / (D / 8), c8 = v % (D / 8);
+    *reinterpret_cast<bf16x8*>(&buf[r * TL::KP + c8 * 8]) = pf.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < TL::VPT; ++i) {
+    const int v = tid + 256 * i;
+    const int r = v / (KT / 8), c8 = v % (KT / 8);
+    *reinterpret_cast<bf16x8*>(&buf[TL::KSZ + r * TL::VP + c8 * 8]) = pf.v[i];
+  }
+}
+
+// S^T for one 32-key sub-block: lane (half, col) gets, for each 32-query block,
+// query col against keys kb*32 + 8*(r/4) + 4*half + r%4, r = 0..15.
+template <int D, int QB, int KT>
+__device__ __forceinline__ void qk_block(f32x16 (&s)[QB], const AttnState<D, QB>& st,
+                                         const bf16* Ks, int kb, int half, int col) {
+  typedef Tile<D, QB, KT> TL;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a =
+        *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * TL::KP + ks * 16 + half * 8]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[qb][ks], s[qb], 0, 0, 0);
+  }
+}
+
+// Online softmax of one 32-key sub-block and O^T += V^T P^T for it.
+template <int D, int QB, int KT, bool MASK>
+__device__ __forceinline__ void softmax_pv_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
+                                                 const bf16* Vs, int kb, int kbase, int T,
+                                                 float c, int half, int col) {
+  typedef Tile<D, QB, KT> TL;
+  if constexpr (MASK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key >= T)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][r] = -INFINITY;
+    }
+  }
+  const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+  bf16x8 pb[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float mx = s[qb][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Lazy rescale: keep a stale max while the new one exceeds it by at most
+    // 2^8 in probability (values stay <= 256, exact after the final O / l).
+    if (__any((mx - st.m[qb]) * c > kLazyLog2)) {
+      const float m_new = fmaxf(st.m[qb], mx);
+      const float alpha = __builtin_amdgcn_exp2f((st.m[qb] - m_new) * c);
+      st.m[qb] = m_new;
+      st.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[qb][db][r] *= alpha;
+    }
+    const float mc = st.m[qb] * c;
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pb[qb][gp][e] =
+            static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[qb][8 * gp + e], c, -mc)));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pb[qb][gp][e], pb[qb][gp][e + 1]};
+        st.l[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l[qb], false);
+      }
+    }
+  }
+  // The B operand element e of MFMA step gp is key kb*32 + 16*gp + 8*(e/4) +
+  // 4*half + e%4; the V^T operand is read with the same key order.
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+    const int kofs = kb * 32 + 16 * gp + 4 * half;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16* vrow = &Vs[(db * 32 + col) * TL::VP + kofs];
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
+      const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][gp], st.o[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+// One key tile for one wave.  The QK^T of sub-block kb+1 is issued before the
+// softmax of sub-block kb so the matrix cores and the VALU work overlap.
+template <int D, int QB, int KT, bool MASK>
+__device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* buf, int k0, int T,
+                                            float c, int half, int col) {
+  typedef Tile<D, QB, KT> TL;
+  const bf16* Ks = buf;
+  const bf16* Vs = buf + TL::KSZ;
+  f32x16 s[2][QB];
+  qk_block<D, QB, KT>(s[0], st, Ks, 0, half, col);
+#pragma unroll
+  for (int kb = 0; kb < TL::NKB; ++kb) {
+    if (kb + 1 < TL::NKB) qk_block<D, QB, KT>(s[(kb + 1) & 1], st, Ks, kb + 1, half, col);
+    softmax_pv_block<D, QB, KT, MASK>(st, s[kb & 1], Vs, kb, k0, T, c, half, col);
+  }
+}
+
+template <int D, int QB, int KT>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams ap) {
-  constexpr int KP = D + 8;   // Ks row pitch (bf16)
-  constexpr int VP = KT + 8;  // Vs row pitch (bf16)
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[D * VP];
+  typedef Tile<D, QB, KT> TL;
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int qtile = blockIdx.x % ap.qtiles;
-  const int bh = blockIdx.x / ap.qtiles;  // b * n + head
+  const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
+  const int qtile = lid % ap.qtiles;
+  const int bh = lid / ap.qtiles;  // b * n + head
   const int head = bh % ap.n, b = bh / ap.n;
   const int T = ap.T;
 
@@ -69,122 +267,66 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams ap) {
   const bf16* K = static_cast<const bf16*>(ap.k) + int64_t(bh) * T * D;
   const bf16* Vt = static_cast<const bf16*>(ap.vt) + int64_t(bh) * D * ap.Tp;
 
-  const int qi = qtile * QT + wave * 32 + col;
+  AttnState<D, QB> st;
   const bf16x8 zero8 = {};
-  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qf[ks] = qi < T ? *reinterpret_cast<const bf16x8*>(Q + int64_t(qi) * D + ks * 16 + half * 8)
-                    : zero8;
-
-  f32x16 o[D / 32];
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qtile * TL::QT + wave * TL::QPW + qb * 32 + col;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sc = ap.scale;
-
-  for (int k0 = 0; k0 < T; k0 += KT) {
-    __syncthreads();  // previous tile fully consumed
-    for (int v = tid; v < KT * D / 8; v += 256) {
-      const int r = v / (D / 8), c8 = v % (D / 8);
-      const int key = k0 + r;
-      bf16x8 val = zero8;
-      if (key < T) val = *reinterpret_cast<const bf16x8*>(K + int64_t(key) * D + c8 * 8);
-      *reinterpret_cast<bf16x8*>(&Ks[r * KP + c8 * 8]) = val;
-    }
-    for (int v = tid; v < D * KT / 8; v += 256) {
-      const int r = v / (KT / 8), c8 = v % (KT / 8);
-      const int key = k0 + c8 * 8;
-      const bf16* src = Vt + int64_t(r) * ap.Tp + key;
-      bf16x8 val;
-      if (key + 8 <= T) {
-        val = *reinterpret_cast<const bf16x8*>(src);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] = key + e < T ? src[e] : static_cast<bf16>(0.f);
-      }
-      *reinterpret_cast<bf16x8*>(&Vs[r * VP + c8 * 8]) = val;
-    }
-    __syncthreads();
-
-    // S^T block: lane (half, col) holds query col, keys kb*32 + 8*(r/4) + 4*half + r%4.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * KP + ks * 16 + half * 8]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
-    }
-    float mx = -INFINITY;
-    const bool tail = k0 + KT > T;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * sc;
-        if (tail) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= T) v = -INFINITY;
-        }
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    for (int ks = 0; ks < D / 16; ++ks)
+      st.qf[qb][ks] = qi < T ? *reinterpret_cast<const bf16x8*>(Q + int64_t(qi) * D + ks * 16 +
+                                                                 half * 8)
+                             : zero8;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) st.o[qb][db][r] = 0.f;
+    st.m[qb] = -INFINITY;
+    st.l[qb] = 0.f;
+  }
+  const float c = ap.scale;
 
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
-        l_run += p;
-        s[kb][r] = p;
-      }
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<bf16>(s[kb][8 * gp + e]);
-        const int kofs = kb * 32 + 16 * gp + 4 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16* vrow = &Vs[(db * 32 + col) * VP + kofs];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
-        }
-      }
-    }
+  const int ntiles = (T + KT - 1) / KT;
+  const int nfull = T / KT;
+  Prefetch<D, QB, KT> pf;
+  if (nfull > 0)
+    load_tile<D, QB, KT, false>(pf, K, Vt, ap.Tp, 0, T, tid);
+  else
+    load_tile<D, QB, KT, true>(pf, K, Vt, ap.Tp, 0, T, tid);
+  store_tile<D, QB, KT>(lds, pf, tid);
+
+  for (int j = 0; j < nfull; ++j) {
+    __syncthreads();  // tile j is in buffer j&1; buffer (j+1)&1 is free
+    const int kn = (j + 1) * KT;
+    if (j + 1 < nfull)
+      load_tile<D, QB, KT, false>(pf, K, Vt, ap.Tp, kn, T, tid);
+    else if (j + 1 < ntiles)
+      load_tile<D, QB, KT, true>(pf, K, Vt, ap.Tp, kn, T, tid);
+    attend_tile<D, QB, KT, false>(st, lds + (j & 1) * TL::BUF, j * KT, T, c, half, col);
+    if (j + 1 < ntiles) store_tile<D, QB, KT>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
+  }
+  if (nfull < ntiles) {  // the partial last tile
+    __syncthreads();
+    attend_tile<D, QB, KT, true>(st, lds + (nfull & 1) * TL::BUF, nfull * KT, T, c, half, col);
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l;
-  if (qi < T) {
-    bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * T + qi) * ap.C + head * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qtile * TL::QT + wave * TL::QPW + qb * 32 + col;
+    const float l = st.l[qb] + __shfl_xor(st.l[qb], 32, 64);
+    const float inv = 1.0f / l;
+    if (qi < T) {
+      bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * T + qi) * ap.C + head * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 pk;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(o[db][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(O + db * 32 + 8 * g + 4 * half) = pk;
-      }
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(st.o[qb][db][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(O + db * 32 + 8 * g + 4 * half) = pk;
+        }
+    }
   }
 }
 
@@ -269,6 +411,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
   }
 }
 
+template <int D, int QB, int KT>
+void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
+  ap.qtiles = int((ap.T + Tile<D, QB, KT>::QT - 1) / Tile<D, QB, KT>::QT);
+  attn_bf16_kernel<D, QB, KT><<<dim3(unsigned(bh * ap.qtiles)), 256, 0, stream>>>(ap);
+}
+
 }  // namespace
 
 hipError_t launch_attention(const Plan& p, const Args& a) {
@@ -285,13 +433,11 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   ap.scale = kLog2e / sqrtf(float(p.d));
   const int64_t bh = p.B * p.n;
   if (p.dtype == SSA_BF16) {
-    ap.qtiles = int((p.T + QT - 1) / QT);
-    dim3 grid(unsigned(bh * ap.qtiles));
     switch (p.d) {
-      case 32: attn_bf16_kernel<32><<<grid, 256, 0, a.stream>>>(ap); break;
-      case 64: attn_bf16_kernel<64><<<grid, 256, 0, a.stream>>>(ap); break;
-      case 96: attn_bf16_kernel<96><<<grid, 256, 0, a.stream>>>(ap); break;
-      default: attn_bf16_kernel<128><<<grid, 256, 0, a.stream>>>(ap); break;
+      case 32: launch_bf16<32, 1, 64>(ap, bh, a.stream); break;
+      case 64: launch_bf16<64, 1, 64>(ap, bh, a.stream); break;
+      case 96: launch_bf16<96, 1, 64>(ap, bh, a.stream); break;
+      default: launch_bf16<128, 1, 64>(ap, bh, a.stream); break;
     }
   } else {
     ap.qtiles = int((p.T + FQT - 1) / FQT);
