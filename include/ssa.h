@@ -42,9 +42,13 @@
  *   gn_partial  float4 (count, mean, M2, 0) per (b, g, split)
  *   gn_stats    float2 (mean, rstd) per (b, g)
  *   gn_coef     float2 (a, s) per (b, c): GN(x)[b,c,t] = a*x[b,c,t] + s
- *   q, k        (B, n, T, d)   dtype, token-major per head
+ *   q, k        (B, n, T, d)   dtype, token-major per head; bf16 q holds
+ *                              Q * log2(e) / sqrt(d) (the score scale)
  *   vt          (B, n, d, Tp)  dtype, V transposed, Tp = T rounded up to 64;
- *                              entries t >= T are never written
+ *                              fp32: token t in column t; bf16: token t in
+ *                              column t with bits 2 and 3 swapped (the order of
+ *                              the attention kernel's MFMA operand); columns of
+ *                              tokens >= T are never written
  *   o           (B, T, C)      dtype, heads concatenated along channels
  * After ssa_forward these hold the block's intermediates for inspection.
  */

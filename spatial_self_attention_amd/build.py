@@ -28,6 +28,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # No kernel relies on NaN semantics (masked scores are -inf, never NaN);
+    # without this every fmaxf first quiets its operands with an extra v_max.
+    "-fno-honor-nans",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -8,7 +8,8 @@
 //     m' = max(m, max_k s_k),  O <- O * 2^(m - m'),  l <- l * 2^(m - m') + sum 2^(s_k - m'),
 //     O <- O + P V,            finally O / l,
 //
-// with the scores in the log2 domain (s = q.k * log2(e) / sqrt(d)).
+// with the scores in the log2 domain (s = q.k * log2(e) / sqrt(d); the bf16
+// path gets Q already multiplied by log2(e) / sqrt(d) from the projection).
 //
 // bf16 kernel (gfx950 MFMA): 4 waves x 32 queries per work-group, key tiles of
 // 64 double-buffered in LDS (the next tile is fetched into registers while the
@@ -22,12 +23,16 @@
 //    MFMA's B operand for O^T += V^T P^T, up to a permutation of the key
 //    index that the V^T operand loads apply identically (a dot product does
 //    not depend on the order of its terms).
-// V is read from the transposed (d, Tp) layout, so each V^T operand is two
-// 8-byte LDS reads.  O is written token-major (B, T, C), heads concatenated.
+// V is read from the transposed (d, Tp) layout whose tokens sit in vt_slot
+// order, so each V^T operand is one conflict-free 16-byte LDS read.  O is
+// written token-major (B, T, C), heads concatenated.
 // The softmax runs per 32-key sub-block; the QK^T MFMAs of the next sub-block
-// are issued before it so matrix-core and VALU work overlap.  O and l are
-// rescaled lazily: only when a row max grows by more than 2^8.  Row sums are
-// taken with v_dot2 over the same bf16-rounded probabilities that enter P V.
+// are issued before it so matrix-core and VALU work overlap.  The running max
+// m is subtracted by the matrix core (the score MFMAs accumulate onto a C
+// operand holding -m), so a probability costs one v_exp, half a v_cvt_pk and
+// half a v_dot2 (the row sum, over the same bf16-rounded values that enter
+// P V).  m is raised lazily, only when a lane's 16 probabilities of a
+// sub-block sum past 2^8; then O and l are rescaled and that sub-block redone.
 //
 // fp32 kernel: 64 queries x 4 lanes per query (each lane owns d/4 dims),
 // FMA only, key tiles of 32 in LDS.
@@ -54,8 +59,20 @@ struct AttnParams {
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLazyLog2 = 8.f;  // rescale O only when the row max grows by more than 2^8
+// A sub-block's probabilities 2^(s - m) are accepted against the running max
+// m while this lane's 16 of them sum to at most 2^8 (so none exceeds 2^8 and
+// the fp32 accumulators stay far from overflow); otherwise m is raised first.
+constexpr float kLazySum = 256.f;
+
+// Word 3 of a raw buffer resource on the gfx9 family: 32-bit data format, no
+// swizzle.  Loads at or past num_records bytes return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
 
 // Work-group id -> logical id so that consecutive logical ids (query tiles of
 // one head, which share K and V) run on the same XCD: work-groups are handed
@@ -63,6 +80,16 @@ constexpr float kLazyLog2 = 8.f;  // rescale O only when the row max grows by mo
 __device__ __forceinline__ int xcd_remap(int w, int nwg) {
   const int q = nwg >> 3, r = nwg & 7, x = w & 7;
   return x * q + min(x, r) + (w >> 3);
+}
+
+// max / sum of v over lanes l and l^32 (one v_permlane32_swap, no LDS)
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, int QB, int KT>
@@ -81,48 +108,45 @@ struct Tile {
 template <int D, int QB>
 struct AttnState {
   bf16x8 qf[QB][D / 16];   // B operand of S^T = K Q^T, one query per lane column
+  f32x16 nm[QB];           // -m in every entry: the C operand the score MFMAs start from
   f32x16 o[QB][D / 32];    // O^T accumulators (d x 32 queries per block)
-  float m[QB];             // running row max, raw score units
+  float m[QB];             // running max, log2 units
   float l[QB];             // running row sum (this lane's half of the keys)
 };
 
 // Registers holding the next K and V^T tiles while the current one is used.
 template <int D, int QB, int KT>
 struct Prefetch {
-  bf16x8 k[Tile<D, QB, KT>::VPT];
-  bf16x8 v[Tile<D, QB, KT>::VPT];
+  u32x4 k[Tile<D, QB, KT>::VPT];
+  u32x4 v[Tile<D, QB, KT>::VPT];
 };
 
-// Global -> registers for one K tile and one V^T tile (keys k0 .. k0+KT-1).
-// MASK: keys >= T read as zero (K rows are clamped to stay inside the head).
+// Global -> registers for one K tile and one V^T tile (keys k0 .. k0+KT-1),
+// through buffer resources based at the tile, so the per-thread offsets are
+// loop-invariant.  K rows >= T lie past num_records and read as zero; MASK
+// zeroes the V^T slots of tokens >= T (their columns are never written).
 template <int D, int QB, int KT, bool MASK>
 __device__ __forceinline__ void load_tile(Prefetch<D, QB, KT>& pf, const bf16* K, const bf16* Vt,
                                           int Tp, int k0, int T, int tid) {
-  const bf16x8 zero8 = {};
+  typedef Tile<D, QB, KT> TL;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + int64_t(k0) * D, int64_t(T - k0) * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vt + k0, (int64_t(D) * Tp - k0) * 2);
 #pragma unroll
-  for (int i = 0; i < Tile<D, QB, KT>::VPT; ++i) {
-    const int v = tid + 256 * i;
-    const int r = v / (D / 8), c8 = v % (D / 8);
-    const int key = k0 + r;
-    if (MASK) {
-      const bf16x8 val =
-          *reinterpret_cast<const bf16x8*>(K + int64_t(min(key, T - 1)) * D + c8 * 8);
-      pf.k[i] = key < T ? val : zero8;
-    } else {
-      pf.k[i] = *reinterpret_cast<const bf16x8*>(K + int64_t(key) * D + c8 * 8);
-    }
-  }
+  for (int i = 0; i < TL::VPT; ++i)
+    pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + 256 * i) * 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < Tile<D, QB, KT>::VPT; ++i) {
+  for (int i = 0; i < TL::VPT; ++i) {
     const int v = tid + 256 * i;
     const int r = v / (KT / 8), c8 = v % (KT / 8);
-    const int key = k0 + c8 * 8;
-    // rows have Tp >= k0 + KT entries, so the vector read stays in the row
-    bf16x8 val = *reinterpret_cast<const bf16x8*>(Vt + int64_t(r) * Tp + key);
-    if (MASK) {
+    u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(vr, (r * Tp + c8 * 8) * 2, 0, 0);
+    if (MASK) {  // slot k0+c8*8+e holds token vt_slot(k0+c8*8+e)
+      const int key = k0 + c8 * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (key + e >= T) val[e] = static_cast<bf16>(0.f);
+      for (int w = 0; w < 4; ++w) {
+        const unsigned lo = vt_slot(key + 2 * w) < T ? 0xffffu : 0u;
+        const unsigned hi = vt_slot(key + 2 * w + 1) < T ? 0xffff0000u : 0u;
+        val[w] &= lo | hi;
+      }
     }
     pf.v[i] = val;
   }
@@ -135,41 +159,62 @@ __device__ __forceinline__ void store_tile(bf16* buf, const Prefetch<D, QB, KT>&
   for (int i = 0; i < TL::VPT; ++i) {
     const int v = tid + 256 * i;
     const int r = v / (D / 8), c8 = v % (D / 8);
-    *reinterpret_cast<bf16x8*>(&buf[r * TL::KP + c8 * 8]) = pf.k[i];
+    *reinterpret_cast<u32x4*>(&buf[r * TL::KP + c8 * 8]) = pf.k[i];
   }
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i) {
     const int v = tid + 256 * i;
     const int r = v / (KT / 8), c8 = v % (KT / 8);
-    *reinterpret_cast<bf16x8*>(&buf[TL::KSZ + r * TL::VP + c8 * 8]) = pf.v[i];
+    *reinterpret_cast<u32x4*>(&buf[TL::KSZ + r * TL::VP + c8 * 8]) = pf.v[i];
   }
 }
 
-// S^T for one 32-key sub-block: lane (half, col) gets, for each 32-query block,
-// query col against keys kb*32 + 8*(r/4) + 4*half + r%4, r = 0..15.
+// S^T - m for one 32-key sub-block: lane (half, col) gets, for each 32-query
+// block, query col against keys kb*32 + 8*(r/4) + 4*half + r%4, r = 0..15.
+// All 16 entries of a lane belong to one query, so the accumulation starts
+// from the C operand nm = (-m, .., -m) and the matrix core subtracts the max.
 template <int D, int QB, int KT>
 __device__ __forceinline__ void qk_block(f32x16 (&s)[QB], const AttnState<D, QB>& st,
                                          const bf16* Ks, int kb, int half, int col) {
   typedef Tile<D, QB, KT> TL;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a =
         *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * TL::KP + ks * 16 + half * 8]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[qb][ks], s[qb], 0, 0, 0);
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[qb][ks], ks == 0 ? st.nm[qb] : s[qb],
+                                                      0, 0, 0);
   }
 }
 
-// Online softmax of one 32-key sub-block and O^T += V^T P^T for it.
+// 2^(s - delta) of one lane's 16 scores, rounded to bf16 in MFMA B-operand
+// order, and their sum (v_dot2 over the rounded values that enter P V).
+__device__ __forceinline__ float probs(bf16x8 (&pb)[2], const f32x16& s, float delta) {
+  const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+  float part = 0.f;
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pb[gp][e] = static_cast<bf16>(__builtin_amdgcn_exp2f(s[8 * gp + e] - delta));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pr = {pb[gp][e], pb[gp][e + 1]};
+      part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part, false);
+    }
+  }
+  return part;
+}
+
+// Online softmax of one 32-key sub-block (scores already relative to m) and
+// O^T += V^T P^T for it.  FIRST: the first sub-block, which sets m.  Returns
+// whether m was raised (wave-uniform), with the raise per query block in delta.
 template <int D, int QB, int KT, bool MASK>
-__device__ __forceinline__ void softmax_pv_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
-                                                 const bf16* Vs, int kb, int kbase, int T,
-                                                 float c, int half, int col) {
+__device__ __forceinline__ bool softmax_pv_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
+                                                 float (&delta)[QB], const bf16* Vs, int kb,
+                                                 int kbase, int T, int half, int col,
+                                                 bool first) {
   typedef Tile<D, QB, KT> TL;
   if constexpr (MASK) {
 #pragma unroll
@@ -180,72 +225,83 @@ __device__ __forceinline__ void softmax_pv_block(AttnState<D, QB>& st, f32x16 (&
         for (int qb = 0; qb < QB; ++qb) s[qb][r] = -INFINITY;
     }
   }
-  const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
   bf16x8 pb[QB][2];
+  float part[QB];
+  bool big = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float mx = s[qb][0];
+    part[qb] = probs(pb[qb], s[qb], 0.f);
+    big = big || !(part[qb] <= kLazySum);
+  }
+  const bool raise = first || __builtin_amdgcn_ballot_w64(big);
+  if (raise) {
+    // Raise m to this sub-block's row max, rescale O and l, and redo the
+    // probabilities.
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescale: keep a stale max while the new one exceeds it by at most
-    // 2^8 in probability (values stay <= 256, exact after the final O / l).
-    if (__any((mx - st.m[qb]) * c > kLazyLog2)) {
-      const float m_new = fmaxf(st.m[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f((st.m[qb] - m_new) * c);
-      st.m[qb] = m_new;
-      st.l[qb] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = s[qb][0];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+      mx = halves_max(mx);
+      const float m_new = first ? mx : fmaxf(st.m[qb], st.m[qb] + mx);
+      delta[qb] = m_new - st.m[qb];
+      if (!first) {
+        const float alpha = __builtin_amdgcn_exp2f(-delta[qb]);
+        st.l[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[qb][db][r] *= alpha;
-    }
-    const float mc = st.m[qb] * c;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int gp = 0; gp < 2; ++gp) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pb[qb][gp][e] =
-            static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[qb][8 * gp + e], c, -mc)));
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pb[qb][gp][e], pb[qb][gp][e + 1]};
-        st.l[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l[qb], false);
+          for (int r = 0; r < 16; ++r) st.o[qb][db][r] *= alpha;
       }
+      st.m[qb] = m_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.nm[qb][r] = -m_new;
+      part[qb] = probs(pb[qb], s[qb], delta[qb]);
     }
   }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) st.l[qb] += part[qb];
   // The B operand element e of MFMA step gp is key kb*32 + 16*gp + 8*(e/4) +
-  // 4*half + e%4; the V^T operand is read with the same key order.
+  // 4*half + e%4; V^T rows hold token t in slot vt_slot(t), which puts those
+  // 8 keys at slots kb*32 + 16*gp + 8*half + e: one 16-byte read.
 #pragma unroll
   for (int gp = 0; gp < 2; ++gp) {
-    const int kofs = kb * 32 + 16 * gp + 4 * half;
+    const int kofs = kb * 32 + 16 * gp + 8 * half;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const bf16* vrow = &Vs[(db * 32 + col) * TL::VP + kofs];
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-      const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[(db * 32 + col) * TL::VP + kofs]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][gp], st.o[qb][db], 0, 0, 0);
     }
   }
+  return raise;
 }
 
 // One key tile for one wave.  The QK^T of sub-block kb+1 is issued before the
-// softmax of sub-block kb so the matrix cores and the VALU work overlap.
+// softmax of sub-block kb so the matrix cores and the VALU work overlap; when
+// that softmax raises m, the scores already formed against the old m are
+// shifted by the raise.
 template <int D, int QB, int KT, bool MASK>
-__device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* buf, int k0, int T,
-                                            float c, int half, int col) {
+__device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* buf, int k0,
+                                            int T, int half, int col, bool first) {
   typedef Tile<D, QB, KT> TL;
   const bf16* Ks = buf;
   const bf16* Vs = buf + TL::KSZ;
   f32x16 s[2][QB];
+  float delta[QB];
   qk_block<D, QB, KT>(s[0], st, Ks, 0, half, col);
 #pragma unroll
   for (int kb = 0; kb < TL::NKB; ++kb) {
     if (kb + 1 < TL::NKB) qk_block<D, QB, KT>(s[(kb + 1) & 1], st, Ks, kb + 1, half, col);
-    softmax_pv_block<D, QB, KT, MASK>(st, s[kb & 1], Vs, kb, k0, T, c, half, col);
+    const bool raised = softmax_pv_block<D, QB, KT, MASK>(st, s[kb & 1], delta, Vs, kb, k0, T, half,
+                                                          col, first && kb == 0);
+    if (kb + 1 < TL::NKB && raised) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[(kb + 1) & 1][qb][r] -= delta[qb];
+    }
   }
 }
 
@@ -278,13 +334,14 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams ap) {
                                                                  half * 8)
                              : zero8;
 #pragma unroll
+    for (int r = 0; r < 16; ++r) st.nm[qb][r] = 0.f;
+#pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[qb][db][r] = 0.f;
-    st.m[qb] = -INFINITY;
+    st.m[qb] = 0.f;
     st.l[qb] = 0.f;
   }
-  const float c = ap.scale;
 
   const int ntiles = (T + KT - 1) / KT;
   const int nfull = T / KT;
@@ -302,19 +359,19 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams ap) {
       load_tile<D, QB, KT, false>(pf, K, Vt, ap.Tp, kn, T, tid);
     else if (j + 1 < ntiles)
       load_tile<D, QB, KT, true>(pf, K, Vt, ap.Tp, kn, T, tid);
-    attend_tile<D, QB, KT, false>(st, lds + (j & 1) * TL::BUF, j * KT, T, c, half, col);
+    attend_tile<D, QB, KT, false>(st, lds + (j & 1) * TL::BUF, j * KT, T, half, col, j == 0);
     if (j + 1 < ntiles) store_tile<D, QB, KT>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
   }
   if (nfull < ntiles) {  // the partial last tile
     __syncthreads();
-    attend_tile<D, QB, KT, true>(st, lds + (nfull & 1) * TL::BUF, nfull * KT, T, c, half, col);
+    attend_tile<D, QB, KT, true>(st, lds + (nfull & 1) * TL::BUF, nfull * KT, T, half, col,
+                                 nfull == 0);
   }
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qtile * TL::QT + wave * TL::QPW + qb * 32 + col;
-    const float l = st.l[qb] + __shfl_xor(st.l[qb], 32, 64);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / halves_sum(st.l[qb]);
     if (qi < T) {
       bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * T + qi) * ap.C + head * D;
 #pragma unroll

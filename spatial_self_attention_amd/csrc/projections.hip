@@ -5,9 +5,12 @@
 // Both are computed in the transposed orientation D = W * Z^T (M = output
 // channels, N = tokens, K = input channels).  With the MFMA output layout a
 // lane then owns one token column and runs of 4 consecutive channels, which
-//  * for Q and K gives 8-byte stores into the token-major (B, n, T, d) layout,
+//  * for Q and K gives 8-byte stores into the token-major (B, n, T, d) layout
+//    (bf16 Q is stored times log2(e) / sqrt(d), the attention kernel's score
+//    scale, folded in before the one rounding),
 //  * for V gives token-contiguous stores into the transposed (B, n, d, Tp)
-//    layout the attention kernel's P*V product reads,
+//    layout the attention kernel's P*V product reads (bf16: tokens in the
+//    vt_slot order of that kernel's MFMA operand),
 //  * for the output projection gives token-contiguous stores straight into
 //    NCHW, so bias + residual + the token-to-image transpose are one epilogue.
 //
@@ -20,6 +23,8 @@
 // bf16: 128x128x64 work-group tiles, 4 waves each owning a 64x64 quadrant as
 // 2x2 v_mfma_f32_32x32x16_bf16 blocks, fp32 accumulation.
 // fp32: 64x64x16 LDS-tiled FMA kernels (no reduced-precision shortcuts).
+#include <math.h>
+
 #include "ssa_internal.h"
 
 namespace ssa {
@@ -39,6 +44,7 @@ struct ProjParams {
   void* out;           // (B, C, T) (kOut)
   int C, T, n, d, Tp;
   int M;               // 3C (kQkv) or C (kOut)
+  float q_scale;       // bf16 Q is stored times log2(e) / sqrt(d) (kQkv)
   int64_t NT;          // B*T tokens
 };
 
@@ -209,16 +215,18 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
           const int head = c / pp.d, dd = c - head * pp.d;
           const int64_t bh = b * pp.n + head;
           if (which < 2) {
+            const float sc = which == 0 ? pp.q_scale : 1.f;
             bf16x4 pk;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(v[e]);
+            for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(v[e] * sc);
             bf16* dst = static_cast<bf16*>(which == 0 ? pp.q : pp.k);
             *reinterpret_cast<bf16x4*>(dst + (bh * T + t) * pp.d + dd) = pk;
           } else {
             bf16* dst = static_cast<bf16*>(pp.vt);
+            const int slot = vt_slot(t);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              dst[(bh * pp.d + dd + e) * pp.Tp + t] = static_cast<bf16>(v[e]);
+              dst[(bh * pp.d + dd + e) * pp.Tp + slot] = static_cast<bf16>(v[e]);
           }
         } else {
           const bf16* x = static_cast<const bf16*>(pp.x);
@@ -360,6 +368,7 @@ ProjParams make_params(const Plan& p, const Args& a, int mode) {
   pp.d = int(p.d);
   pp.Tp = int(p.Tp);
   pp.M = mode == kQkv ? int(3 * p.C) : int(p.C);
+  pp.q_scale = 1.4426950408889634f / sqrtf(float(p.d));
   pp.NT = p.B * p.T;
   return pp;
 }

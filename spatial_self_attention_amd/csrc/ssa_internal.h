@@ -19,6 +19,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kGnEps = 1e-5f;
 constexpr int kTokPad = 64;  // vt row pitch is T rounded up to this
 
+// Slot of token t in a bf16 V^T row: bits 2 and 3 of t are swapped, so in
+// every run of 16 tokens the groups 4..7 and 8..11 trade places.  That puts
+// the 8 keys one lane of v_mfma_f32_32x32x16_bf16 multiplies in one B-operand
+// step (4*half + {0..3} and 8 + 4*half + {0..3}) next to each other, so the
+// attention kernel reads its V^T operand with one 16-byte LDS load.  The map
+// is its own inverse and stays inside each run of 16 (and inside Tp).
+__host__ __device__ __forceinline__ int vt_slot(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
 // Everything a launch needs, derived once from the sizes by make_plan().
 struct Plan {
   int64_t B, C, H, W, G, n;

@@ -96,7 +96,12 @@ def test_stage_parity(wl):
     q, _ = region(ws, wl, "q", edt, (B, n, T, d))
     k, _ = region(ws, wl, "k", edt, (B, n, T, d))
     vt, _ = region(ws, wl, "vt", edt, (B, n, d, lay["t_pad"]))
+    if wl.dtype == "bf16":  # bf16 V^T columns hold token t at t with bits 2 and 3 swapped
+        t = np.arange(lay["t_pad"])
+        vt = vt[..., (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1)]
     o, _ = region(ws, wl, "o", edt, (B, T, C))
+    if wl.dtype == "bf16":  # bf16 q holds Q times the score scale log2(e) / sqrt(d)
+        q = q / (np.log2(np.e) / np.sqrt(d))
     assert err(q, heads(st["Q"]), wl.dtype if wl.dtype == "bf16" else "f32") <= tol
     assert err(k, heads(st["K"]), wl.dtype) <= tol
     assert err(vt[..., :T], heads(st["V"]).transpose(0, 1, 3, 2), wl.dtype) <= tol
