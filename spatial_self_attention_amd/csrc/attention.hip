@@ -30,8 +30,7 @@
 // are issued before it so matrix-core and VALU work overlap.  The running max
 // m is subtracted by the matrix core (the score MFMAs accumulate onto a C
 // operand holding -m), so a probability costs one v_exp, half a v_cvt_pk and
-// half a v_dot2 (the row sum, over the same bf16-rounded values that enter
-// P V).  m is raised lazily, only when a lane's 16 probabilities of a
+// one v_add (the row sum).  m is raised lazily, only when a lane's 16 probabilities of a
 // sub-block sum past 2^8; then O and l are rescaled and that sub-block redone.
 //
 // fp32 kernel: 64 queries x 4 lanes per query (each lane owns d/4 dims),
@@ -189,22 +188,20 @@ __device__ __forceinline__ void qk_block(f32x16 (&s)[QB], const AttnState<D, QB>
 }
 
 // 2^(s - delta) of one lane's 16 scores, rounded to bf16 in MFMA B-operand
-// order, and their sum (v_dot2 over the rounded values that enter P V).
+// order, and their fp32 sum.  The sum uses plain adds (two chains): v_add
+// issues in the shadow of the matrix core, while v_dot2 stalls it.
 __device__ __forceinline__ float probs(bf16x8 (&pb)[2], const f32x16& s, float delta) {
-  const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
-  float part = 0.f;
+  float part[2] = {0.f, 0.f};
 #pragma unroll
   for (int gp = 0; gp < 2; ++gp) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      pb[gp][e] = static_cast<bf16>(__builtin_amdgcn_exp2f(s[8 * gp + e] - delta));
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 pr = {pb[gp][e], pb[gp][e + 1]};
-      part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part, false);
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(s[8 * gp + e] - delta);
+      part[e & 1] += p;
+      pb[gp][e] = static_cast<bf16>(p);
     }
   }
-  return part;
+  return part[0] + part[1];
 }
 
 // Online softmax of one 32-key sub-block (scores already relative to m) and

@@ -243,6 +243,399 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernels, main path (C % 64 == 0 and T % 4 == 0)
+//
+// 128 x 128 x 64 work-group tiles, double-buffered in LDS: the next k-step is
+// fetched into registers (and for Q/K/V normalised) while the current one
+// feeds the MFMAs, then written to the other buffer; one barrier per k-step.
+// Each wave owns a 64 x 64 quadrant as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.
+// The orientation of a wave's product follows its store layout:
+//  * Q and K (token-major): D = W Z^T, a lane holds 4 consecutive channels of
+//    one token -> 8-byte stores into (B, n, T, d);
+//  * V (V^T rows) and the output projection (NCHW rows): D = Z W^T (operands
+//    swapped), a lane holds 4 consecutive tokens of one channel -> 8-byte
+//    stores of 4 V^T slots (vt_slot keeps aligned runs of 4 together) or of 4
+//    pixels of one output channel, with the residual read the same way.
+// Work-group ids are remapped so the m-tiles of one token tile (which share
+// the x / O rows they read) run on the same XCD and share its L2.
+// ---------------------------------------------------------------------------
+constexpr int GM = 128, GN = 128, GK = 64;
+constexpr int GP = GK + 8;  // LDS row pitch (bf16): 144-byte rows, conflict-free 16-byte reads
+
+// Word 3 of a raw buffer resource on the gfx9 family (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ bf16x8 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Work-group id -> logical id: work-groups go to the 8 XCDs round-robin, so
+// XCD x receives ids x, x+8, ...; consecutive logical ids land on one XCD.
+__device__ __forceinline__ int xcd_remap_gemm(int w, int nwg) {
+  const int q = nwg >> 3, r = nwg & 7, x = w & 7;
+  return x * q + min(x, r) + (w >> 3);
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// One k-step of A (weight rows) and B in registers, as loaded: for the QKV
+// projection B is raw x (8 channel rows x 4 tokens) plus the 8 (a, s) GN
+// coefficients of those channels, normalised only when written to LDS so that
+// the loads stay in flight behind the current step's MFMAs.
+struct Stage {
+  bf16x8 a[4];
+  bf16x8 b[4];     // kOut: 4 token rows of O
+  u32x2 xr[8];     // kQkv: x rows, 4 bf16 tokens each
+  f32x4 cf[4];     // kQkv: (a, s) of the 8 channels
+};
+
+// Loop-invariant addressing of one thread's loads: buffer resources and
+// per-thread byte offsets are fixed; each k-step only moves a scalar offset.
+//  A: vector i = tid + 256 i is row (tid >> 3) + 32 i, channels (tid & 7) * 8;
+//     the 32 rows of one i lie in one 64-row block, so they belong to one of
+//     Wq / Wk / Wv (C % 64 == 0) and the resource is uniform.
+//  B (Q/K/V): thread = (token quad tq, channel octet co), 8 channel rows of 4
+//     tokens each.  Lanes are laid out so that each group of 16 lanes stores
+//     its 16-byte LDS vectors to 16 distinct bank groups, while 16 lanes of
+//     one channel row still read 128 contiguous bytes of x.
+//  B (out projection): vector i is token row (tid >> 3) + 32 i of O.
+// Rows past M and tokens past B*T are clamped onto valid ones: they only feed
+// accumulator rows / columns that the epilogue never stores.
+struct LoadCtx {
+  __amdgpu_buffer_rsrc_t ra[4];
+  int sa[4];       // scalar byte offset of row block i in its weight
+  int va;          // per-thread byte offset inside a row block
+  __amdgpu_buffer_rsrc_t rb, rc;
+  int vb[4];       // kOut: byte offset of token row i in O
+  int vx, vc;      // kQkv: byte offsets of x[b][co*8][t] and coef[b][co*8]
+  int xrow;        // kQkv: bytes between consecutive channel rows of x (2T)
+};
+
+__device__ __forceinline__ int qkv_tq(int tid) {
+  return (tid & 3) | (((tid >> 4) & 7) << 2);
+}
+__device__ __forceinline__ int qkv_co(int tid) { return ((tid >> 2) & 3) | ((tid >> 7) << 2); }
+
+template <int MODE>
+__device__ __forceinline__ void gemm_setup(LoadCtx& lc, const ProjParams& pp, int m0, int n0,
+                                           int tid) {
+  const int C = pp.C;
+  const uint32_t wbytes = uint32_t(C) * uint32_t(C) * 2u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rb = m0 + 32 * i < pp.M ? m0 + 32 * i : 0;
+    const int which = MODE == kQkv ? rb / C : 0;
+    lc.ra[i] = make_rsrc(pp.w[which], wbytes);
+    lc.sa[i] = (rb - which * C) * C * 2;
+  }
+  lc.va = ((tid >> 3) * C + (tid & 7) * 8) * 2;
+  if constexpr (MODE == kOut) {
+    lc.rb = make_rsrc(pp.o, uint32_t(pp.NT) * uint32_t(C) * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nn = min(n0 + (tid >> 3) + 32 * i, pp.NT - 1);
+      lc.vb[i] = (nn * C + (tid & 7) * 8) * 2;
+    }
+  } else {
+    const int T = pp.T;
+    const int tq = qkv_tq(tid), co = qkv_co(tid);
+    const int nn = min(n0 + tq * 4, pp.NT - 4);
+    const int b = int(unsigned(nn) / unsigned(T));
+    const int t = nn - b * T;
+    lc.rb = make_rsrc(pp.x, uint32_t(pp.NT) * uint32_t(C) * 2u);
+    lc.rc = make_rsrc(pp.coef, uint32_t(pp.NT / T) * uint32_t(C) * 8u);
+    lc.vx = ((b * C + co * 8) * T + t) * 2;
+    lc.vc = (b * C + co * 8) * 8;
+    lc.xrow = T * 2;
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void gemm_load(Stage& sg, const LoadCtx& lc, int k0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sg.a[i] = ld16(lc.ra[i], lc.va, lc.sa[i] + k0 * 2);
+  if constexpr (MODE == kOut) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sg.b[i] = ld16(lc.rb, lc.vb[i], k0 * 2);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      sg.cf[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lc.rc, lc.vc + 16 * q, k0 * 8, 0));
+    const int sx = k0 * lc.xrow;  // k0 channel rows further down
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sg.xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(lc.rb, lc.vx + j * lc.xrow, sx, 0));
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void gemm_store(bf16* As, bf16* Bs, const Stage& sg, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = tid + 256 * i;
+    *reinterpret_cast<bf16x8*>(&As[(v >> 3) * GP + (v & 7) * 8]) = sg.a[i];
+  }
+  if constexpr (MODE == kOut) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + 256 * i;
+      *reinterpret_cast<bf16x8*>(&Bs[(v >> 3) * GP + (v & 7) * 8]) = sg.b[i];
+    }
+  } else {
+    // GN(x) = a x + s in fp32, rounded once to bf16; b[e] = token e's 8 channels
+    bf16x8 b[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = sg.cf[j >> 1][(j & 1) * 2], sh = sg.cf[j >> 1][(j & 1) * 2 + 1];
+      const u32x2 v = sg.xr[j];
+      const float xv[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                           __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e][j] = static_cast<bf16>(fmaf(a, xv[e], sh));
+    }
+    const int tq = qkv_tq(tid), co = qkv_co(tid);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<bf16x8*>(&Bs[(tq * 4 + e) * GP + co * 8]) = b[e];
+  }
+}
+
+template <bool TR>
+__device__ __forceinline__ void gemm_compute(f32x16 (&acc)[2][2], const bf16* As, const bf16* Bs,
+                                             int wm, int wn, int half, int col) {
+#pragma unroll
+  for (int s = 0; s < GK / 16; ++s) {
+    const int kofs = s * 16 + half * 8;
+    bf16x8 fa[2], fb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + col) * GP + kofs]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + col) * GP + kofs]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// acc[i][j]: channel block i x token block j of the wave's quadrant.
+// TR = false: rows are channels; TR = true: rows are tokens.
+// The loads of k-step s+1 are issued right after the barrier of step s and
+// land in LDS (normalised, for Q/K/V) after step s's MFMAs.
+template <int MODE, bool TR>
+__device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], const ProjParams& pp, bf16* lds,
+                                          int m0, int n0, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  LoadCtx lc;
+  gemm_setup<MODE>(lc, pp, m0, n0, tid);
+  const int nk = pp.C / GK;  // >= 1
+  constexpr int BUF = (GM + GN) * GP;
+  Stage sg;
+  gemm_load<MODE>(sg, lc, 0);
+  gemm_store<MODE>(lds, lds + GM * GP, sg, tid);
+  for (int ks = 0; ks < nk; ++ks) {
+    __syncthreads();  // buffer ks&1 is complete; buffer (ks+1)&1 is no longer read
+    if (ks + 1 < nk) gemm_load<MODE>(sg, lc, (ks + 1) * GK);
+    const bf16* As = lds + (ks & 1) * BUF;
+    gemm_compute<TR>(acc, As, As + GM * GP, wm, wn, half, col);
+    if (ks + 1 < nk) {
+      bf16* Ad = lds + ((ks + 1) & 1) * BUF;
+      gemm_store<MODE>(Ad, Ad + GM * GP, sg, tid);
+    }
+  }
+}
+
+// Epilogue: each wave stages its 64 x 64 quadrant in its own LDS region in
+// the destination's layout (bias added; Q scaled), then stores it with
+// coalesced vectors.
+//  * Q / K: E[token][channel] bf16; a lane stores 16-byte runs of 8 channels
+//    of one token, 8 lanes covering one token's 64 channels.
+//  * V: E[channel][token] bf16; a lane owns one run of 4 tokens and stores it
+//    (4 consecutive V^T slots) for 16 channels, 16 lanes per channel row.
+//  * output: E[channel][token] fp32 (so x + Y is rounded once), same lanes,
+//    with the residual read in the same 8-byte runs.
+// Staging pitches (elements): 144-byte bf16 rows and 272-byte fp32 rows keep
+// the 8- and 16-byte staging writes of 16 lanes on distinct banks.
+constexpr int EPB = 72, EPF = 68;
+
+struct EpiCtx {
+  int mw, nw;            // first row / token of the wave's quadrant
+  int lane, half, col;
+};
+
+template <int MODE, bool TR>
+__device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const ProjParams& pp,
+                                          bf16* lds, int wave, const EpiCtx& ec) {
+  const int C = pp.C, half = ec.half, col = ec.col;
+  if constexpr (MODE == kOut) {
+    float* E = reinterpret_cast<float*>(lds) + wave * 64 * EPF;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cl = i * 32 + col;
+      const float bias = static_cast<float>(static_cast<const bf16*>(pp.bias[0])[ec.mw + cl]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + bias;
+          *reinterpret_cast<f32x4*>(&E[cl * EPF + j * 32 + 8 * g + 4 * half]) = v;
+        }
+    }
+  } else if constexpr (TR) {  // V
+    bf16* E = lds + wave * 64 * EPB;
+    const bf16* bias = static_cast<const bf16*>(pp.bias[2]) + (ec.mw - 2 * C);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cl = i * 32 + col;
+      const float bv = static_cast<float>(bias[cl]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(acc[i][j][4 * g + e] + bv);
+          *reinterpret_cast<bf16x4*>(&E[cl * EPB + j * 32 + 8 * g + 4 * half]) = pk;
+        }
+    }
+  } else {  // Q or K
+    bf16* E = lds + wave * 64 * EPB;
+    const int which = ec.mw / C;
+    const float sc = which == 0 ? pp.q_scale : 1.f;
+    const bf16* bias = static_cast<const bf16*>(pp.bias[which]) + (ec.mw - which * C);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cl = i * 32 + 8 * g + 4 * half;
+        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(bias + cl);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bf16x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = static_cast<bf16>((acc[i][j][4 * g + e] + static_cast<float>(bv[e])) * sc);
+          *reinterpret_cast<bf16x4*>(&E[(j * 32 + col) * EPB + cl]) = pk;
+        }
+      }
+  }
+}
+
+template <int MODE, bool TR>
+__device__ __forceinline__ void epi_store(const ProjParams& pp, const bf16* lds, int wave,
+                                          const EpiCtx& ec) {
+  const int C = pp.C, T = pp.T, lane = ec.lane;
+  if constexpr (MODE == kOut || TR) {
+    const int tq = lane & 15;  // this lane's run of 4 tokens
+    const int nn = ec.nw + 4 * tq;
+    if (nn >= pp.NT) return;   // NT % 4 == 0: a run is all in or all out
+    const int b = int(unsigned(nn) / unsigned(T));
+    const int t = nn - b * T;
+    if constexpr (MODE == kOut) {
+      const float* E = reinterpret_cast<const float*>(lds) + wave * 64 * EPF;
+      const bf16* x = static_cast<const bf16*>(pp.x);
+      bf16* out = static_cast<bf16*>(pp.out);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int cl = 4 * u + (lane >> 4);
+        const int64_t idx = (int64_t(b) * C + ec.mw + cl) * T + t;
+        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(x + idx);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(&E[cl * EPF + 4 * tq]);
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(static_cast<float>(xv[e]) + y[e]);
+        *reinterpret_cast<bf16x4*>(out + idx) = pk;
+      }
+    } else {
+      const bf16* E = lds + wave * 64 * EPB;
+      bf16* vt = static_cast<bf16*>(pp.vt);
+      const int slot = vt_slot(t);  // aligned runs of 4 tokens keep their order
+      const int cw = ec.mw - 2 * C;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int cl = 4 * u + (lane >> 4);
+        const int c = cw + cl;
+        const int head = int(unsigned(c) / unsigned(pp.d)), dd = c - head * pp.d;
+        *reinterpret_cast<bf16x4*>(vt + (int64_t(b * pp.n + head) * pp.d + dd) * pp.Tp + slot) =
+            *reinterpret_cast<const bf16x4*>(&E[cl * EPB + 4 * tq]);
+      }
+    }
+  } else {
+    const bf16* E = lds + wave * 64 * EPB;
+    const int which = ec.mw / C;
+    bf16* dst = static_cast<bf16*>(which == 0 ? pp.q : pp.k);
+    const int q8 = lane & 7;  // this lane's 8-channel run
+    const int c = ec.mw - which * C + q8 * 8;
+    const int head = int(unsigned(c) / unsigned(pp.d)), dd = c - head * pp.d;
+    const int r0 = lane >> 3;
+    int nn = ec.nw + r0;
+    int b = int(unsigned(min(nn, pp.NT - 1)) / unsigned(T));
+    int t = nn - b * T;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // token r0 + 8u
+      if (u > 0) {
+        nn += 8;
+        t += 8;
+        while (t >= T) { t -= T; ++b; }
+      }
+      if (nn < pp.NT)
+        *reinterpret_cast<bf16x8*>(dst + (int64_t(b * pp.n + head) * T + t) * pp.d + dd) =
+            *reinterpret_cast<const bf16x8*>(&E[(r0 + 8 * u) * EPB + q8 * 8]);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(ProjParams pp, int mtiles) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (GM + GN) * GP];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lid = xcd_remap_gemm(int(blockIdx.x), int(gridDim.x));
+  const int m0 = (lid % mtiles) * GM;
+  const int n0 = (lid / mtiles) * GN;
+  EpiCtx ec;
+  ec.mw = m0 + (wave >> 1) * 64;
+  ec.nw = n0 + (wave & 1) * 64;
+  ec.lane = lane;
+  ec.half = lane >> 5;
+  ec.col = lane & 31;
+  // V rows and the output projection take the swapped orientation
+  const bool tr = MODE == kOut || ec.mw >= 2 * pp.C;
+  const bool valid = ec.mw < pp.M;  // false for the upper half of a 64-row last tile
+  f32x16 acc[2][2];
+  if (tr) {
+    gemm_main<MODE, true>(acc, pp, lds, m0, n0, tid);
+    __syncthreads();  // every wave is done reading the operand tiles
+    if (valid) epi_stage<MODE, true>(acc, pp, lds, wave, ec);
+    __syncthreads();
+    if (valid) epi_store<MODE, true>(pp, lds, wave, ec);
+  } else {
+    gemm_main<MODE, false>(acc, pp, lds, m0, n0, tid);
+    __syncthreads();
+    if (valid) epi_stage<MODE, false>(acc, pp, lds, wave, ec);
+    __syncthreads();
+    if (valid) epi_store<MODE, false>(pp, lds, wave, ec);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 FMA kernels
 // ---------------------------------------------------------------------------
 constexpr int FM = 64, FN = 64, FK = 16, FP = 64 + 4;
@@ -376,7 +769,11 @@ ProjParams make_params(const Plan& p, const Args& a, int mode) {
 template <int MODE>
 hipError_t launch_mode(const Plan& p, const Args& a) {
   const ProjParams pp = make_params(p, a, MODE);
-  if (p.dtype == SSA_BF16) {
+  if (p.dtype == SSA_BF16 && p.C % 64 == 0 && p.T % 4 == 0) {
+    const int mtiles = int((pp.M + GM - 1) / GM);
+    const int64_t ntiles = (pp.NT + GN - 1) / GN;
+    gemm_bf16_kernel<MODE><<<dim3(unsigned(mtiles * ntiles)), 256, 0, a.stream>>>(pp, mtiles);
+  } else if (p.dtype == SSA_BF16) {
     dim3 grid(unsigned((pp.NT + BN - 1) / BN), unsigned((pp.M + BM - 1) / BM));
     if (MODE == kOut || p.T % 4 != 0)
       proj_bf16_kernel<MODE, false><<<grid, 256, 0, a.stream>>>(pp);
