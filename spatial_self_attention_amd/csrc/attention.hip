@@ -168,51 +168,94 @@ __device__ __forceinline__ void store_tile(bf16* buf, const Prefetch<D, QB, KT>&
   }
 }
 
+// Operand fragments of one 32-key sub-block, read from LDS one pipeline
+// step before the MFMAs that use them (the LDS latency is then hidden behind
+// a step of MFMA and softmax work instead of stalling each MFMA).
+template <int D>
+struct KFrag {  // A operand of S^T = K Q^T: keys kb*32 + col, dims ks*16 + half*8 ..
+  bf16x8 a[D / 16];
+};
+template <int D>
+struct VFrag {  // A operand of O^T += V^T P^T: dims db*32 + col, keys per step gp
+  bf16x8 a[2][D / 32];
+};
+
+template <int D, int QB, int KT>
+__device__ __forceinline__ void read_k(KFrag<D>& f, const bf16* Ks, int kb, int half, int col) {
+  typedef Tile<D, QB, KT> TL;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    f.a[ks] = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * TL::KP + ks * 16 + half * 8]);
+}
+
+// The B operand element e of MFMA step gp is key kb*32 + 16*gp + 8*(e/4) +
+// 4*half + e%4; V^T rows hold token t in slot vt_slot(t), which puts those 8
+// keys at slots kb*32 + 16*gp + 8*half + e: one 16-byte read.
+template <int D, int QB, int KT>
+__device__ __forceinline__ void read_v(VFrag<D>& f, const bf16* Vs, int kb, int half, int col) {
+  typedef Tile<D, QB, KT> TL;
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      f.a[gp][db] = *reinterpret_cast<const bf16x8*>(
+          &Vs[(db * 32 + col) * TL::VP + kb * 32 + 16 * gp + 8 * half]);
+}
+
 // S^T - m for one 32-key sub-block: lane (half, col) gets, for each 32-query
 // block, query col against keys kb*32 + 8*(r/4) + 4*half + r%4, r = 0..15.
 // All 16 entries of a lane belong to one query, so the accumulation starts
 // from the C operand nm = (-m, .., -m) and the matrix core subtracts the max.
-template <int D, int QB, int KT>
-__device__ __forceinline__ void qk_block(f32x16 (&s)[QB], const AttnState<D, QB>& st,
-                                         const bf16* Ks, int kb, int half, int col) {
-  typedef Tile<D, QB, KT> TL;
+template <int D, int QB>
+__device__ __forceinline__ void qk_mfma(f32x16 (&s)[QB], const AttnState<D, QB>& st,
+                                        const KFrag<D>& f) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 a =
-        *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * TL::KP + ks * 16 + half * 8]);
+  for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[qb][ks], ks == 0 ? st.nm[qb] : s[qb],
-                                                      0, 0, 0);
-  }
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks], st.qf[qb][ks],
+                                                      ks == 0 ? st.nm[qb] : s[qb], 0, 0, 0);
+}
+
+// O^T += V^T P^T for one sub-block.
+template <int D, int QB>
+__device__ __forceinline__ void pv_mfma(AttnState<D, QB>& st, const bf16x8 (&pb)[QB][2],
+                                        const VFrag<D>& f) {
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[gp][db], pb[qb][gp], st.o[qb][db], 0, 0, 0);
 }
 
 // 2^(s - delta) of one lane's 16 scores, rounded to bf16 in MFMA B-operand
 // order, and their fp32 sum.  The sum uses plain adds (two chains): v_add
 // issues in the shadow of the matrix core, while v_dot2 stalls it.
 __device__ __forceinline__ float probs(bf16x8 (&pb)[2], const f32x16& s, float delta) {
-  float part[2] = {0.f, 0.f};
+  float p[16];
 #pragma unroll
-  for (int gp = 0; gp < 2; ++gp) {
+  for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - delta);
+  float part[2] = {p[0], p[1]};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(s[8 * gp + e] - delta);
-      part[e & 1] += p;
-      pb[gp][e] = static_cast<bf16>(p);
-    }
-  }
+  for (int r = 2; r < 16; ++r) part[r & 1] += p[r];
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[gp][e] = static_cast<bf16>(p[8 * gp + e]);
   return part[0] + part[1];
 }
 
-// Online softmax of one 32-key sub-block (scores already relative to m) and
-// O^T += V^T P^T for it.  FIRST: the first sub-block, which sets m.  Returns
-// whether m was raised (wave-uniform), with the raise per query block in delta.
+// Online softmax of one 32-key sub-block (scores already relative to m):
+// the bf16 probabilities in MFMA B-operand order and the row-sum update.
+// FIRST: the first sub-block, which sets m.  Returns whether m was raised
+// (wave-uniform), with the raise per query block in delta; O is rescaled
+// after the P V products already issued for earlier sub-blocks.
 template <int D, int QB, int KT, bool MASK>
-__device__ __forceinline__ bool softmax_pv_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
-                                                 float (&delta)[QB], const bf16* Vs, int kb,
-                                                 int kbase, int T, int half, int col,
-                                                 bool first) {
-  typedef Tile<D, QB, KT> TL;
+__device__ __forceinline__ bool softmax_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
+                                              bf16x8 (&pb)[QB][2], float (&delta)[QB], int kb,
+                                              int kbase, int T, int half, bool first) {
   if constexpr (MASK) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -222,7 +265,6 @@ __device__ __forceinline__ bool softmax_pv_block(AttnState<D, QB>& st, f32x16 (&
         for (int qb = 0; qb < QB; ++qb) s[qb][r] = -INFINITY;
     }
   }
-  bf16x8 pb[QB][2];
   float part[QB];
   bool big = false;
 #pragma unroll
@@ -258,48 +300,47 @@ __device__ __forceinline__ bool softmax_pv_block(AttnState<D, QB>& st, f32x16 (&
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) st.l[qb] += part[qb];
-  // The B operand element e of MFMA step gp is key kb*32 + 16*gp + 8*(e/4) +
-  // 4*half + e%4; V^T rows hold token t in slot vt_slot(t), which puts those
-  // 8 keys at slots kb*32 + 16*gp + 8*half + e: one 16-byte read.
-#pragma unroll
-  for (int gp = 0; gp < 2; ++gp) {
-    const int kofs = kb * 32 + 16 * gp + 8 * half;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[(db * 32 + col) * TL::VP + kofs]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][gp], st.o[qb][db], 0, 0, 0);
-    }
-  }
   return raise;
 }
 
-// One key tile for one wave.  The QK^T of sub-block kb+1 is issued before the
-// softmax of sub-block kb so the matrix cores and the VALU work overlap; when
-// that softmax raises m, the scores already formed against the old m are
-// shifted by the raise.
+// One key tile for one wave, software-pipelined over its 32-key sub-blocks.
+// Step kb runs the softmax of sub-block kb on the VALU while the matrix core
+// works on QK^T of sub-block kb+1 and P V of sub-block kb-1; the LDS operand
+// fragments those MFMAs need were read during step kb-1, and step kb reads
+// the fragments of step kb+1 (K of kb+2, V of kb).  When the softmax raises
+// m, the scores of kb+1 (formed against the old m) are shifted by the raise.
 template <int D, int QB, int KT, bool MASK>
 __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* buf, int k0,
                                             int T, int half, int col, bool first) {
   typedef Tile<D, QB, KT> TL;
+  constexpr int NKB = TL::NKB;
   const bf16* Ks = buf;
   const bf16* Vs = buf + TL::KSZ;
   f32x16 s[2][QB];
+  bf16x8 pb[2][QB][2];
   float delta[QB];
-  qk_block<D, QB, KT>(s[0], st, Ks, 0, half, col);
+  KFrag<D> kf[2];
+  VFrag<D> vf[2];
+  read_k<D, QB, KT>(kf[0], Ks, 0, half, col);
+  if (NKB > 1) read_k<D, QB, KT>(kf[1], Ks, 1, half, col);
+  qk_mfma<D, QB>(s[0], st, kf[0]);
 #pragma unroll
-  for (int kb = 0; kb < TL::NKB; ++kb) {
-    if (kb + 1 < TL::NKB) qk_block<D, QB, KT>(s[(kb + 1) & 1], st, Ks, kb + 1, half, col);
-    const bool raised = softmax_pv_block<D, QB, KT, MASK>(st, s[kb & 1], delta, Vs, kb, k0, T, half,
-                                                          col, first && kb == 0);
-    if (kb + 1 < TL::NKB && raised) {
+  for (int kb = 0; kb < NKB; ++kb) {
+    // fragments for the next step: K of kb+2, V of kb
+    if (kb + 2 < NKB) read_k<D, QB, KT>(kf[kb & 1], Ks, kb + 2, half, col);
+    read_v<D, QB, KT>(vf[kb & 1], Vs, kb, half, col);
+    if (kb + 1 < NKB) qk_mfma<D, QB>(s[(kb + 1) & 1], st, kf[(kb + 1) & 1]);
+    if (kb > 0) pv_mfma<D, QB>(st, pb[(kb - 1) & 1], vf[(kb - 1) & 1]);
+    const bool raised = softmax_block<D, QB, KT, MASK>(st, s[kb & 1], pb[kb & 1], delta, kb, k0, T,
+                                                       half, first && kb == 0);
+    if (kb + 1 < NKB && raised) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[(kb + 1) & 1][qb][r] -= delta[qb];
     }
   }
+  pv_mfma<D, QB>(st, pb[(NKB - 1) & 1], vf[(NKB - 1) & 1]);
 }
 
 template <int D, int QB, int KT>
