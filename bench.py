@@ -60,10 +60,10 @@ def stage_work(wl):
 
 # Kernel names (as rocprofv3 prints them) behind each stage, for the counters.
 STAGE_KERNELS = {
-    "gn_stats": "gn_partial_kernel",
-    "qkv": "proj_bf16_kernel<0",
+    "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
+    "qkv": "gemm_bf16_kernel<0>",
     "attention": "attn_bf16_kernel",
-    "out_proj": "proj_bf16_kernel<1",
+    "out_proj": "gemm_bf16_kernel<1>",
 }
 
 
@@ -116,7 +116,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--graph", action="store_true",
                     help="time K steps replayed from one HIP graph instead of eager launches")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 10 device-to-device copies of BYTES each (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to HBM bytes)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 10}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the block runs on a single MI355X here; "
               "run with --gpus 1", file=sys.stderr)

@@ -319,16 +319,40 @@ __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* bu
   f32x16 s[2][QB];
   bf16x8 pb[2][QB][2];
   float delta[QB];
+  if constexpr (MASK) {
+    // The partial last tile: only its sub-blocks that hold keys < T, one at a
+    // time (the tile is visited once per work-group).
+    const int nv = min(NKB, (T - k0 + 31) / 32);
+    for (int kb = 0; kb < nv; ++kb) {
+      KFrag<D> kf;
+      VFrag<D> vf;
+      read_k<D, QB, KT>(kf, Ks, kb, half, col);
+      qk_mfma<D, QB>(s[0], st, kf);
+      softmax_block<D, QB, KT, true>(st, s[0], pb[0], delta, kb, k0, T, half, first && kb == 0);
+      read_v<D, QB, KT>(vf, Vs, kb, half, col);
+      pv_mfma<D, QB>(st, pb[0], vf);
+    }
+    return;
+  }
+  // Wide heads (d > 64) read their fragments in the step that uses them:
+  // their MFMA work per step is twice as long, and two fragment sets would
+  // not fit beside the accumulators.
+  constexpr bool kAhead = D <= 64;
   KFrag<D> kf[2];
   VFrag<D> vf[2];
   read_k<D, QB, KT>(kf[0], Ks, 0, half, col);
-  if (NKB > 1) read_k<D, QB, KT>(kf[1], Ks, 1, half, col);
+  if (kAhead && NKB > 1) read_k<D, QB, KT>(kf[1], Ks, 1, half, col);
   qk_mfma<D, QB>(s[0], st, kf[0]);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    // fragments for the next step: K of kb+2, V of kb
-    if (kb + 2 < NKB) read_k<D, QB, KT>(kf[kb & 1], Ks, kb + 2, half, col);
-    read_v<D, QB, KT>(vf[kb & 1], Vs, kb, half, col);
+    if (kAhead) {
+      // fragments for the next step: K of kb+2, V of kb
+      if (kb + 2 < NKB) read_k<D, QB, KT>(kf[kb & 1], Ks, kb + 2, half, col);
+      read_v<D, QB, KT>(vf[kb & 1], Vs, kb, half, col);
+    } else {
+      if (kb + 1 < NKB) read_k<D, QB, KT>(kf[(kb + 1) & 1], Ks, kb + 1, half, col);
+      if (kb > 0) read_v<D, QB, KT>(vf[(kb - 1) & 1], Vs, kb - 1, half, col);
+    }
     if (kb + 1 < NKB) qk_mfma<D, QB>(s[(kb + 1) & 1], st, kf[(kb + 1) & 1]);
     if (kb > 0) pv_mfma<D, QB>(st, pb[(kb - 1) & 1], vf[(kb - 1) & 1]);
     const bool raised = softmax_block<D, QB, KT, MASK>(st, s[kb & 1], pb[kb & 1], delta, kb, k0, T,
@@ -340,11 +364,17 @@ __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* bu
         for (int r = 0; r < 16; ++r) s[(kb + 1) & 1][qb][r] -= delta[qb];
     }
   }
+  if (!kAhead) read_v<D, QB, KT>(vf[(NKB - 1) & 1], Vs, NKB - 1, half, col);
   pv_mfma<D, QB>(st, pb[(NKB - 1) & 1], vf[(NKB - 1) & 1]);
 }
 
+// Three work-groups per CU (12 waves) for the narrow heads; the wide heads
+// need more registers and run two.
+template <int D>
+constexpr int attn_min_blocks() { return D <= 64 ? 3 : 2; }
+
 template <int D, int QB, int KT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnParams ap) {
+__global__ __launch_bounds__(256, attn_min_blocks<D>()) void attn_bf16_kernel(AttnParams ap) {
   typedef Tile<D, QB, KT> TL;
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF];
 
