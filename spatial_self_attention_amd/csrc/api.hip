@@ -39,17 +39,23 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
   p->dtype = dtype;
   p->esize = dtype == SSA_F32 ? 4 : 2;
 
-  // Statistics split: aim for about 2048 work-groups over the whole input,
-  // with at least 2048 elements per work-group.
+  // Statistics split.  With enough (b, g) segments to fill the chip and
+  // segments a work-group streams quickly, one work-group per segment also
+  // finalises the statistics (one kernel).  Otherwise each segment is cut into
+  // chunks of at least 8192 elements, about 2048 work-groups in all, and a
+  // second kernel merges them.
   const int64_t L = (C / G) * T;
   const int vec = 16 / p->esize;
   p->gn_vec = (L % vec == 0) ? vec : 1;
   p->seg_len = L;
   int64_t segs = B * G;
-  int64_t want = (2048 + segs - 1) / segs;
-  int64_t cap = (L + 2047) / 2048;
-  int64_t splits = want < cap ? want : cap;
-  if (splits < 1) splits = 1;
+  int64_t splits = 1;
+  if (segs < 256 || L > 65536) {
+    const int64_t want = (2048 + segs - 1) / segs;
+    const int64_t cap = (L + 8191) / 8192;
+    splits = want < cap ? want : cap;
+    if (splits < 1) splits = 1;
+  }
   int64_t chunk = (L + splits - 1) / splits;
   chunk = (chunk + p->gn_vec - 1) / p->gn_vec * p->gn_vec;
   p->chunk = chunk;

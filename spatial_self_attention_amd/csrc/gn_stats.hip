@@ -2,18 +2,21 @@
 // num_groups groups, eps 1e-5, affine norm_weight / norm_bias).
 //
 // Group g of sample b is channels g*C/G .. (g+1)*C/G-1 over all pixels, which
-// in NCHW is ONE contiguous run of (C/G)*T elements.  The pass is HBM-bound:
+// in NCHW is ONE contiguous run of (C/G)*T elements.  The pass is HBM-bound.
 //
-//   gn_partial_kernel   grid B*G*splits: each work-group streams one chunk
-//                       of a segment with 16-byte loads and produces
-//                       (count, mean, M2) of that chunk.  Per vector the mean
-//                       and M2 are formed two-pass in registers, then merged
-//                       with Chan's pairwise update (thread -> wave -> block).
-//   gn_finalize_kernel  grid (B*G): one wave merges the chunks of a segment,
-//                       forms mean and rstd = 1/sqrt(M2/count + eps) (biased
-//                       variance), and emits per-channel coefficients
-//                       a = gamma*rstd, s = beta - mean*a, so that the
-//                       projection prologue normalises with one FMA.
+//   gn_stats_kernel<FINAL>  grid B*G*splits: each work-group streams one chunk
+//       of a segment with 16-byte loads (four in flight per thread).  A thread
+//       accumulates shifted sums, d = x - x0 with x0 the chunk's first element
+//       (sum d and sum d^2: no division in the loop, and little cancellation
+//       because x0 is a sample of the same data); the (count, mean, M2) of the
+//       threads are then merged with Chan's pairwise update (wave -> block).
+//       FINAL (one chunk per segment): the same work-group forms mean and
+//       rstd = 1/sqrt(M2/count + eps) (biased variance) and the per-channel
+//       coefficients a = gamma*rstd, s = beta - mean*a, so that the projection
+//       prologue normalises with one FMA.  Otherwise it writes its chunk's
+//       (count, mean, M2) and
+//   gn_finalize_kernel      grid B*G: one wave merges the chunks of a segment
+//       and emits the same statistics and coefficients.
 #include "ssa_internal.h"
 
 namespace ssa {
@@ -56,54 +59,95 @@ struct VecOf<float, 4> { typedef f32x4 type; };
 template <>
 struct VecOf<bf16, 8> { typedef bf16x8 type; };
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(256) void gn_partial_kernel(const T* __restrict__ x,
-                                                         float4* __restrict__ partial,
-                                                         int64_t seg_len, int64_t chunk,
-                                                         int splits) {
+// mean / rstd of one segment and its per-channel coefficients (all threads
+// of the work-group call it; threads 0.. write).
+template <typename T>
+__device__ __forceinline__ void finalize(Moments m, int seg, const T* __restrict__ gamma,
+                                         const T* __restrict__ beta, float2* __restrict__ stats,
+                                         float2* __restrict__ coef, int G, int Cg, int C,
+                                         int tid, int nthreads) {
+  const float var = m.m2 / m.n;
+  const float rstd = 1.0f / sqrtf(var + kGnEps);
+  if (tid == 0) stats[seg] = make_float2(m.mean, rstd);
+  const int b = seg / G, g = seg % G;
+  for (int c = tid; c < Cg; c += nthreads) {
+    const int ch = g * Cg + c;
+    const float a = to_f32(gamma[ch]) * rstd;
+    coef[int64_t(b) * C + ch] = make_float2(a, to_f32(beta[ch]) - m.mean * a);
+  }
+}
+
+template <typename T, int VEC, bool FINAL>
+__global__ __launch_bounds__(256) void gn_stats_kernel(const T* __restrict__ x,
+                                                       float4* __restrict__ partial,
+                                                       int64_t seg_len, int64_t chunk, int splits,
+                                                       const T* __restrict__ gamma,
+                                                       const T* __restrict__ beta,
+                                                       float2* __restrict__ stats,
+                                                       float2* __restrict__ coef, int G, int Cg,
+                                                       int C) {
+  const int tid = threadIdx.x;
   const int s = int(blockIdx.x % unsigned(splits));
   const int64_t seg = blockIdx.x / unsigned(splits);
   const int64_t begin = int64_t(s) * chunk;
   const int64_t end = min(begin + chunk, seg_len);
   const T* base = x + seg * seg_len;
-  Moments acc{0.f, 0.f, 0.f};
+  const float x0 = to_f32(base[begin]);
+  float sd = 0.f, sq = 0.f;
+  int64_t cnt = 0;
   if constexpr (VEC > 1) {
     typedef typename VecOf<T, VEC>::type V;
     const V* vb = reinterpret_cast<const V*>(base);
-    for (int64_t i = begin / VEC + threadIdx.x; i < end / VEC; i += 256) {
-      V v = vb[i];
-      float f[VEC];
-      float sum = 0.f;
+    const int64_t v0 = begin / VEC, v1 = end / VEC;
+    int64_t i = v0 + tid;
+    for (; i + 3 * 256 < v1; i += 4 * 256) {  // four independent 16-byte loads in flight
+      V v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = vb[i + u * 256];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float d = to_f32(v[u][e]) - x0;
+          sd += d;
+          sq = fmaf(d, d, sq);
+        }
+      cnt += 4 * VEC;
+    }
+    for (; i < v1; i += 256) {
+      const V v = vb[i];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        f[e] = to_f32(v[e]);
-        sum += f[e];
+        const float d = to_f32(v[e]) - x0;
+        sd += d;
+        sq = fmaf(d, d, sq);
       }
-      Moments m;
-      m.n = float(VEC);
-      m.mean = sum * (1.f / VEC);
-      m.m2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) m.m2 += (f[e] - m.mean) * (f[e] - m.mean);
-      acc = merge(acc, m);
+      cnt += VEC;
     }
   } else {
-    for (int64_t i = begin + threadIdx.x; i < end; i += 256) {
-      Moments m{1.f, to_f32(base[i]), 0.f};
-      acc = merge(acc, m);
+    for (int64_t i = begin + tid; i < end; i += 256) {
+      const float d = to_f32(base[i]) - x0;
+      sd += d;
+      sq = fmaf(d, d, sq);
+      ++cnt;
     }
+  }
+  Moments acc{0.f, 0.f, 0.f};
+  if (cnt > 0) {
+    const float n = float(cnt);
+    const float md = sd / n;
+    acc = Moments{n, x0 + md, fmaxf(sq - sd * md, 0.f)};
   }
   acc = wave_merge(acc);
   __shared__ Moments waves[4];
-  const int wave = threadIdx.x / 64;
-  if ((threadIdx.x & 63) == 0) waves[wave] = acc;
+  const int wave = tid / 64;
+  if ((tid & 63) == 0) waves[wave] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    Moments r = waves[0];
-    r = merge(r, waves[1]);
-    r = merge(r, waves[2]);
-    r = merge(r, waves[3]);
-    partial[seg * splits + s] = make_float4(r.n, r.mean, r.m2, 0.f);
+  Moments r = merge(merge(waves[0], waves[1]), merge(waves[2], waves[3]));
+  if constexpr (FINAL) {
+    finalize<T>(r, int(seg), gamma, beta, stats, coef, G, Cg, C, tid, 256);
+  } else {
+    if (tid == 0) partial[seg * splits + s] = make_float4(r.n, r.mean, r.m2, 0.f);
   }
 }
 
@@ -122,37 +166,38 @@ __global__ __launch_bounds__(64) void gn_finalize_kernel(const float4* __restric
     acc = merge(acc, Moments{q.x, q.y, q.z});
   }
   acc = wave_merge(acc);
-  const float var = acc.m2 / acc.n;
-  const float rstd = 1.0f / sqrtf(var + kGnEps);
-  if (lane == 0) stats[seg] = make_float2(acc.mean, rstd);
-  const int b = seg / G, g = seg % G;
-  for (int c = lane; c < Cg; c += 64) {
-    const int ch = g * Cg + c;
-    const float a = to_f32(gamma[ch]) * rstd;
-    coef[int64_t(b) * C + ch] = make_float2(a, to_f32(beta[ch]) - acc.mean * a);
-  }
+  finalize<T>(acc, seg, gamma, beta, stats, coef, G, Cg, C, lane, 64);
 }
 
-template <typename T>
-hipError_t launch_typed(const Plan& p, const Args& a) {
+template <typename T, int VEC>
+hipError_t launch_vec(const Plan& p, const Args& a) {
   const T* x = static_cast<const T*>(a.x);
   float4* partial = reinterpret_cast<float4*>(a.ws + p.ws.gn_partial);
   float2* stats = reinterpret_cast<float2*>(a.ws + p.ws.gn_stats);
   float2* coef = reinterpret_cast<float2*>(a.ws + p.ws.gn_coef);
+  const T* gamma = static_cast<const T*>(a.norm_weight);
+  const T* beta = static_cast<const T*>(a.norm_bias);
+  const int G = int(p.G), Cg = int(p.C / p.G), C = int(p.C);
   dim3 grid(unsigned(p.splits * p.B * p.G));
-  constexpr int kVec = 16 / sizeof(T);
-  if (p.gn_vec == kVec)
-    gn_partial_kernel<T, kVec><<<grid, 256, 0, a.stream>>>(x, partial, p.seg_len, p.chunk,
-                                                           int(p.splits));
-  else
-    gn_partial_kernel<T, 1><<<grid, 256, 0, a.stream>>>(x, partial, p.seg_len, p.chunk,
-                                                        int(p.splits));
+  if (p.splits == 1) {
+    gn_stats_kernel<T, VEC, true><<<grid, 256, 0, a.stream>>>(x, partial, p.seg_len, p.chunk, 1,
+                                                              gamma, beta, stats, coef, G, Cg, C);
+    return hipGetLastError();
+  }
+  gn_stats_kernel<T, VEC, false><<<grid, 256, 0, a.stream>>>(x, partial, p.seg_len, p.chunk,
+                                                             int(p.splits), gamma, beta, stats,
+                                                             coef, G, Cg, C);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   gn_finalize_kernel<T><<<dim3(unsigned(p.B * p.G)), 64, 0, a.stream>>>(
-      partial, int(p.splits), static_cast<const T*>(a.norm_weight),
-      static_cast<const T*>(a.norm_bias), stats, coef, int(p.G), int(p.C / p.G), int(p.C));
+      partial, int(p.splits), gamma, beta, stats, coef, G, Cg, C);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_typed(const Plan& p, const Args& a) {
+  constexpr int kVec = 16 / sizeof(T);
+  return p.gn_vec == kVec ? launch_vec<T, kVec>(p, a) : launch_vec<T, 1>(p, a);
 }
 
 }  // namespace

@@ -154,6 +154,10 @@ EDGE_CASES = [
     # one channel per group (G = C), and C = 320 with 5 heads
     Workload("G=C bf16", "bf16", 2, 64, 6, 6, 64, 2),
     Workload("C320 n5 small", "bf16", 2, 320, 9, 9, 32, 5),
+    # C above the register-resident projection path (768 channels, d = 128)
+    Workload("C768 n6 bf16", "bf16", 2, 768, 6, 10, 32, 6),
+    # one 64-channel chunk (C = 64) with a ragged token block
+    Workload("C64 T=300 bf16", "bf16", 1, 64, 12, 25, 4, 2),
     # fp32 with head sizes that are not a multiple of 4 or 32
     Workload("fp32 d=3", "f32", 2, 6, 4, 5, 3, 2),
     Workload("fp32 d=100", "f32", 1, 200, 3, 7, 8, 2),
