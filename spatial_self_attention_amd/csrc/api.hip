@@ -13,6 +13,22 @@ constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;  // per tensor, for 32-bit
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Compute units of the current device, cached per device (256 when no device
+// can be queried, e.g. for workspace sizing on a host without a GPU).
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
 bool supported_head(int dtype, int64_t d) {
   if (dtype == SSA_F32) return d >= 1 && d <= 128;
   return d == 32 || d == 64 || d == 96 || d == 128;
@@ -38,6 +54,7 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
   p->Tp = (T + kTokPad - 1) / kTokPad * kTokPad;
   p->dtype = dtype;
   p->esize = dtype == SSA_F32 ? 4 : 2;
+  p->cus = device_cus();
 
   // Statistics split.  With enough (b, g) segments to fill the chip and
   // segments a work-group streams quickly, one work-group per segment also

@@ -91,17 +91,19 @@ __device__ __forceinline__ float halves_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int QB, int KT>
+template <int D, int QB, int KT, int NW = 4>
 struct Tile {
   static constexpr int QPW = 32 * QB;      // queries per wave
-  static constexpr int QT = 4 * QPW;       // queries per work-group (4 waves)
+  static constexpr int QT = NW * QPW;      // queries per work-group (NW waves)
+  static constexpr int NTHR = 64 * NW;     // threads per work-group
   static constexpr int NKB = KT / 32;      // 32-key sub-blocks per tile
   static constexpr int KP = D + 8;         // K tile row pitch (bf16)
   static constexpr int VP = KT + 8;        // V^T tile row pitch (bf16)
   static constexpr int KSZ = KT * KP;      // K tile (bf16 elements)
   static constexpr int VSZ = D * VP;       // V^T tile
   static constexpr int BUF = KSZ + VSZ;
-  static constexpr int VPT = KT * D / 8 / 256;  // 16-byte vectors per thread per operand
+  static constexpr int VPT = KT * D / 8 / NTHR;  // 16-byte vectors per thread per operand
+  static_assert(VPT * NTHR == KT * D / 8, "tile vectors must split evenly over the threads");
 };
 
 template <int D, int QB>
@@ -114,28 +116,28 @@ struct AttnState {
 };
 
 // Registers holding the next K and V^T tiles while the current one is used.
-template <int D, int QB, int KT>
+template <int D, int QB, int KT, int NW>
 struct Prefetch {
-  u32x4 k[Tile<D, QB, KT>::VPT];
-  u32x4 v[Tile<D, QB, KT>::VPT];
+  u32x4 k[Tile<D, QB, KT, NW>::VPT];
+  u32x4 v[Tile<D, QB, KT, NW>::VPT];
 };
 
 // Global -> registers for one K tile and one V^T tile (keys k0 .. k0+KT-1),
 // through buffer resources based at the tile, so the per-thread offsets are
 // loop-invariant.  K rows >= T lie past num_records and read as zero; MASK
 // zeroes the V^T slots of tokens >= T (their columns are never written).
-template <int D, int QB, int KT, bool MASK>
-__device__ __forceinline__ void load_tile(Prefetch<D, QB, KT>& pf, const bf16* K, const bf16* Vt,
+template <int D, int QB, int KT, int NW, bool MASK>
+__device__ __forceinline__ void load_tile(Prefetch<D, QB, KT, NW>& pf, const bf16* K, const bf16* Vt,
                                           int Tp, int k0, int T, int tid) {
-  typedef Tile<D, QB, KT> TL;
+  typedef Tile<D, QB, KT, NW> TL;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + int64_t(k0) * D, int64_t(T - k0) * D * 2);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vt + k0, (int64_t(D) * Tp - k0) * 2);
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i)
-    pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + 256 * i) * 16, 0, 0);
+    pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + TL::NTHR * i) * 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i) {
-    const int v = tid + 256 * i;
+    const int v = tid + TL::NTHR * i;
     const int r = v / (KT / 8), c8 = v % (KT / 8);
     u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(vr, (r * Tp + c8 * 8) * 2, 0, 0);
     if (MASK) {  // slot k0+c8*8+e holds token vt_slot(k0+c8*8+e)
@@ -151,18 +153,18 @@ __device__ __forceinline__ void load_tile(Prefetch<D, QB, KT>& pf, const bf16* K
   }
 }
 
-template <int D, int QB, int KT>
-__device__ __forceinline__ void store_tile(bf16* buf, const Prefetch<D, QB, KT>& pf, int tid) {
-  typedef Tile<D, QB, KT> TL;
+template <int D, int QB, int KT, int NW>
+__device__ __forceinline__ void store_tile(bf16* buf, const Prefetch<D, QB, KT, NW>& pf, int tid) {
+  typedef Tile<D, QB, KT, NW> TL;
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i) {
-    const int v = tid + 256 * i;
+    const int v = tid + TL::NTHR * i;
     const int r = v / (D / 8), c8 = v % (D / 8);
     *reinterpret_cast<u32x4*>(&buf[r * TL::KP + c8 * 8]) = pf.k[i];
   }
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i) {
-    const int v = tid + 256 * i;
+    const int v = tid + TL::NTHR * i;
     const int r = v / (KT / 8), c8 = v % (KT / 8);
     *reinterpret_cast<u32x4*>(&buf[TL::KSZ + r * TL::VP + c8 * 8]) = pf.v[i];
   }
@@ -368,14 +370,64 @@ __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* bu
   pv_mfma<D, QB>(st, pb[(NKB - 1) & 1], vf[(NKB - 1) & 1]);
 }
 
+// Per-wave state for queries qbase + 32 qb + col: Q fragments, zero O, m, l.
+template <int D, int QB>
+__device__ __forceinline__ void init_state(AttnState<D, QB>& st, const bf16* Q, int qbase, int T,
+                                           int half, int col) {
+  const bf16x8 zero8 = {};
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qbase + qb * 32 + col;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      st.qf[qb][ks] = qi < T ? *reinterpret_cast<const bf16x8*>(Q + int64_t(qi) * D + ks * 16 +
+                                                                 half * 8)
+                             : zero8;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.nm[qb][r] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[qb][db][r] = 0.f;
+    st.m[qb] = 0.f;
+    st.l[qb] = 0.f;
+  }
+}
+
+// O = O^T accumulators / l, token-major (B, T, C) with heads concatenated.
+template <int D, int QB>
+__device__ __forceinline__ void write_o(const AttnState<D, QB>& st, const AttnParams& ap, int b,
+                                        int head, int qbase, int half, int col) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qbase + qb * 32 + col;
+    const float inv = 1.0f / halves_sum(st.l[qb]);
+    if (qi < ap.T) {
+      bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * ap.T + qi) * ap.C + head * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(st.o[qb][db][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(O + db * 32 + 8 * g + 4 * half) = pk;
+        }
+    }
+  }
+}
+
 // Three work-groups per CU (12 waves) for the narrow heads; the wide heads
 // need more registers and run two.
 template <int D>
 constexpr int attn_min_blocks() { return D <= 64 ? 3 : 2; }
 
-template <int D, int QB, int KT>
-__global__ __launch_bounds__(256, attn_min_blocks<D>()) void attn_bf16_kernel(AttnParams ap) {
-  typedef Tile<D, QB, KT> TL;
+// NW = 4: 128 queries per work-group, several work-groups per CU.  NW = 8:
+// 256 queries per work-group, used for short sequences (T <= 256, one
+// work-group per (sample, head)) so that K and V are read once per head.
+template <int D, int QB, int KT, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? attn_min_blocks<D>() : 1) void attn_bf16_kernel(AttnParams ap) {
+  typedef Tile<D, QB, KT, NW> TL;
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF];
 
   const int tid = threadIdx.x;
@@ -392,43 +444,26 @@ __global__ __launch_bounds__(256, attn_min_blocks<D>()) void attn_bf16_kernel(At
   const bf16* Vt = static_cast<const bf16*>(ap.vt) + int64_t(bh) * D * ap.Tp;
 
   AttnState<D, QB> st;
-  const bf16x8 zero8 = {};
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qtile * TL::QT + wave * TL::QPW + qb * 32 + col;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      st.qf[qb][ks] = qi < T ? *reinterpret_cast<const bf16x8*>(Q + int64_t(qi) * D + ks * 16 +
-                                                                 half * 8)
-                             : zero8;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.nm[qb][r] = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[qb][db][r] = 0.f;
-    st.m[qb] = 0.f;
-    st.l[qb] = 0.f;
-  }
+  init_state<D, QB>(st, Q, qtile * TL::QT + wave * TL::QPW, T, half, col);
 
   const int ntiles = (T + KT - 1) / KT;
   const int nfull = T / KT;
-  Prefetch<D, QB, KT> pf;
+  Prefetch<D, QB, KT, NW> pf;
   if (nfull > 0)
-    load_tile<D, QB, KT, false>(pf, K, Vt, ap.Tp, 0, T, tid);
+    load_tile<D, QB, KT, NW, false>(pf, K, Vt, ap.Tp, 0, T, tid);
   else
-    load_tile<D, QB, KT, true>(pf, K, Vt, ap.Tp, 0, T, tid);
-  store_tile<D, QB, KT>(lds, pf, tid);
+    load_tile<D, QB, KT, NW, true>(pf, K, Vt, ap.Tp, 0, T, tid);
+  store_tile<D, QB, KT, NW>(lds, pf, tid);
 
   for (int j = 0; j < nfull; ++j) {
     __syncthreads();  // tile j is in buffer j&1; buffer (j+1)&1 is free
     const int kn = (j + 1) * KT;
     if (j + 1 < nfull)
-      load_tile<D, QB, KT, false>(pf, K, Vt, ap.Tp, kn, T, tid);
+      load_tile<D, QB, KT, NW, false>(pf, K, Vt, ap.Tp, kn, T, tid);
     else if (j + 1 < ntiles)
-      load_tile<D, QB, KT, true>(pf, K, Vt, ap.Tp, kn, T, tid);
+      load_tile<D, QB, KT, NW, true>(pf, K, Vt, ap.Tp, kn, T, tid);
     attend_tile<D, QB, KT, false>(st, lds + (j & 1) * TL::BUF, j * KT, T, half, col, j == 0);
-    if (j + 1 < ntiles) store_tile<D, QB, KT>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
+    if (j + 1 < ntiles) store_tile<D, QB, KT, NW>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
   }
   if (nfull < ntiles) {  // the partial last tile
     __syncthreads();
@@ -436,23 +471,7 @@ __global__ __launch_bounds__(256, attn_min_blocks<D>()) void attn_bf16_kernel(At
                                  nfull == 0);
   }
 
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qtile * TL::QT + wave * TL::QPW + qb * 32 + col;
-    const float inv = 1.0f / halves_sum(st.l[qb]);
-    if (qi < T) {
-      bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * T + qi) * ap.C + head * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(st.o[qb][db][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(O + db * 32 + 8 * g + 4 * half) = pk;
-        }
-    }
-  }
+  write_o<D, QB>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -536,10 +555,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
   }
 }
 
-template <int D, int QB, int KT>
+template <int D, int QB, int KT, int NW>
 void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
-  ap.qtiles = int((ap.T + Tile<D, QB, KT>::QT - 1) / Tile<D, QB, KT>::QT);
-  attn_bf16_kernel<D, QB, KT><<<dim3(unsigned(bh * ap.qtiles)), 256, 0, stream>>>(ap);
+  typedef Tile<D, QB, KT, NW> TL;
+  ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
+  attn_bf16_kernel<D, QB, KT, NW><<<dim3(unsigned(bh * ap.qtiles)), TL::NTHR, 0, stream>>>(ap);
 }
 
 }  // namespace
@@ -558,11 +578,19 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   ap.scale = kLog2e / sqrtf(float(p.d));
   const int64_t bh = p.B * p.n;
   if (p.dtype == SSA_BF16) {
+    // one 256-query work-group per head when the heads alone fill the chip
+    const bool wide = p.T <= 256 && bh >= p.cus;
     switch (p.d) {
-      case 32: launch_bf16<32, 1, 64>(ap, bh, a.stream); break;
-      case 64: launch_bf16<64, 1, 64>(ap, bh, a.stream); break;
-      case 96: launch_bf16<96, 1, 64>(ap, bh, a.stream); break;
-      default: launch_bf16<128, 1, 64>(ap, bh, a.stream); break;
+      case 32: launch_bf16<32, 1, 64, 4>(ap, bh, a.stream); break;
+      case 64:
+        if (wide) launch_bf16<64, 1, 64, 8>(ap, bh, a.stream);
+        else launch_bf16<64, 1, 64, 4>(ap, bh, a.stream);
+        break;
+      case 96: launch_bf16<96, 1, 64, 4>(ap, bh, a.stream); break;
+      default:
+        if (wide) launch_bf16<128, 1, 64, 8>(ap, bh, a.stream);
+        else launch_bf16<128, 1, 64, 4>(ap, bh, a.stream);
+        break;
     }
   } else {
     ap.qtiles = int((p.T + FQT - 1) / FQT);

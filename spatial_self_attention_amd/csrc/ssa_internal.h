@@ -39,6 +39,7 @@ struct Plan {
   // elements is cut into `splits` chunks of `chunk` elements.
   int64_t seg_len, chunk, splits;
   int gn_vec;      // elements per vector load in the stats pass (1 = scalar)
+  int cus;         // compute units of the current device (launch shaping)
   ssa_workspace_layout ws;
 };
 

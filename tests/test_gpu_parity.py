@@ -154,7 +154,10 @@ EDGE_CASES = [
     # one channel per group (G = C), and C = 320 with 5 heads
     Workload("G=C bf16", "bf16", 2, 64, 6, 6, 64, 2),
     Workload("C320 n5 small", "bf16", 2, 320, 9, 9, 32, 5),
-    # C above the register-resident projection path (768 channels, d = 128)
+    # >= 256 (sample, head) pairs with T <= 256: one 256-query attention work-group per head
+    Workload("wide heads d64 T=64", "bf16", 64, 256, 8, 8, 32, 4),
+    Workload("wide heads d128 T=100", "bf16", 64, 512, 10, 10, 32, 4),
+    # C above 640 channels (768, d = 128)
     Workload("C768 n6 bf16", "bf16", 2, 768, 6, 10, 32, 6),
     # one 64-channel chunk (C = 64) with a ragged token block
     Workload("C64 T=300 bf16", "bf16", 1, 64, 12, 25, 4, 2),
