@@ -1,5 +1,6 @@
 """fp64 CPU oracle of the spatial self-attention block (test infrastructure only)."""
 from .ssa_oracle import (  # noqa: F401
-    EPS, PARAM_KEYS, attention, check_args, forward, forward_pixels,
-    forward_stages, group_norm, image, linear, softmax_keys, tokens,
+    BIAS_KEYS, EPS, PARAM_KEYS, attend, attention, check_args, check_options, forward,
+    forward_pixels, forward_stages, group_norm, image, linear, merge_heads, qk_norm,
+    rel_pos_bias, rope, rope_angles, softmax_keys, split_heads, tokens,
 )
