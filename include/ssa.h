@@ -25,6 +25,10 @@
  *     out_weight                      (C, C)         (out, in)
  *     q_bias, k_bias, v_bias, out_bias (C,)
  *   Every pointer must be 16-byte aligned.
+ * - Biases are nullable: a NULL q_bias, k_bias, v_bias or out_bias is a
+ *   projection without a bias (the HNDL attention operator's qkv_bias /
+ *   out_bias flags: "a projection built without a bias has no bias
+ *   parameter").  Every other data pointer is required.
  * - The caller owns every buffer, including `workspace`.  The library
  *   allocates no device memory and keeps no state between calls; calls on
  *   different streams with different workspaces may run concurrently.
@@ -64,7 +68,7 @@ extern "C" {
 
 typedef enum {
   SSA_OK = 0,
-  SSA_E_NULL = 1,         /* a required pointer is NULL                         */
+  SSA_E_NULL = 1,         /* a required pointer is NULL (biases may be NULL)   */
   SSA_E_SHAPE = 2,        /* a size is negative, or C < 1                       */
   SSA_E_CONSTRAINT = 3,   /* num_groups or num_heads < 1 or does not divide C   */
   SSA_E_DTYPE = 4,        /* unknown dtype code                                 */
@@ -140,6 +144,47 @@ ssa_status ssa_forward_stage(int stage,
                              int64_t B, int64_t C, int64_t H, int64_t W,
                              int64_t num_groups, int64_t num_heads, int dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Optional steps of ssa_forward_ex, each off when its field is NULL / 0.
+ * Order: projections, query/key normalisation, rotary embedding, scaled
+ * scores plus the relative-position bias, softmax, P V.
+ *
+ *  rel_pos_table  ((2H-1)*(2W-1), num_heads), dtype of x: learned 2-D
+ *                 relative-position bias added to the scaled logits (HNDL
+ *                 attention operator, "Relative position bias"): for query q
+ *                 and key k at rows q/W, k/W and columns q%W, k%W,
+ *                 bias[head, q, k] = table[(dy)*(2W-1) + dx, head] with
+ *                 dy = row(q)-row(k)+H-1, dx = col(q)-col(k)+W-1.
+ *  q_norm_gamma,  (num_heads, d) each, dtype of x, both or neither
+ *  k_norm_gamma   (SSA_E_CONSTRAINT otherwise): per-head query/key
+ *                 normalisation (vit-pytorch simple_vit_with_qk_norm.py,
+ *                 RMSNorm): x / max(||x||_2, 1e-12) * sqrt(d) * gamma[head];
+ *                 the scores are then not divided by sqrt(d).
+ *  rope           nonzero: rotary embeddings over the token index t (HNDL
+ *                 attention operator, "Rotary embeddings"): rotate-half over
+ *                 the full head, theta_i = 10000^(-2i/d) and angle t*theta_i
+ *                 in float32; needs an even d (SSA_E_UNSUPPORTED otherwise).
+ * The library reads these tensors during the call's kernels and keeps no
+ * reference; they must not overlap out or the workspace (SSA_E_ALIAS). */
+typedef struct {
+  const void* rel_pos_table;
+  const void* q_norm_gamma;
+  const void* k_norm_gamma;
+  int32_t rope;
+} ssa_options;
+
+/* ssa_forward with optional steps (options may be NULL: the plain block).
+ * Same workspace, validation and stream semantics as ssa_forward. */
+ssa_status ssa_forward_ex(const void* x, void* out,
+                          const void* norm_weight, const void* norm_bias,
+                          const void* q_weight, const void* k_weight,
+                          const void* v_weight, const void* out_weight,
+                          const void* q_bias, const void* k_bias,
+                          const void* v_bias, const void* out_bias,
+                          int64_t B, int64_t C, int64_t H, int64_t W,
+                          int64_t num_groups, int64_t num_heads, int dtype,
+                          const ssa_options* options,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* ssa_status_string(int status);

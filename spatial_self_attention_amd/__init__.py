@@ -15,9 +15,9 @@ from __future__ import annotations
 import torch
 
 from ._binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, PARAM_ORDER, SSA_BF16, SSA_F32, STAGES, SSAError, SSAValueError,
-    lib, ssa_forward, ssa_forward_stage, ssa_get_workspace_layout, ssa_status_string,
-    ssa_workspace_size,
+    BIAS_KEYS, EXPORTS, LIB_PATH, PARAM_ORDER, SSA_BF16, SSA_F32, STAGES, Options, SSAError,
+    SSAValueError, lib, ssa_forward, ssa_forward_ex, ssa_forward_stage, ssa_get_workspace_layout,
+    ssa_status_string, ssa_workspace_size,
 )
 from ._binding import _raise
 
@@ -30,8 +30,8 @@ def dtype_code(dtype: torch.dtype) -> int:
     return _DTYPES[dtype]
 
 
-def _ptr(t: torch.Tensor) -> int:
-    return t.data_ptr() if t.numel() else 0
+def _ptr(t) -> int:
+    return 0 if t is None or t.numel() == 0 else t.data_ptr()
 
 
 def _check_tensors(x: torch.Tensor, params: dict):
@@ -44,6 +44,8 @@ def _check_tensors(x: torch.Tensor, params: dict):
     C = x.shape[1]
     for k in PARAM_ORDER:
         p = params[k]
+        if p is None and k in BIAS_KEYS:
+            continue  # a projection without a bias
         want = (C,) if (k.endswith("_bias") or k.startswith("norm")) else (C, C)
         if tuple(p.shape) != want:
             raise ValueError(f"{k} must have shape {want}, got {tuple(p.shape)}")
@@ -62,31 +64,65 @@ def workspace_for(x: torch.Tensor, num_groups: int, num_heads: int) -> torch.Ten
     return torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
 
 
+def make_options(x, num_heads, rel_pos_table=None, q_norm_gamma=None, k_norm_gamma=None,
+                 rope=False):
+    """An Options structure for the optional steps, or None when none is on.
+
+    rel_pos_table ((2H-1)(2W-1), num_heads), q_norm_gamma / k_norm_gamma
+    (num_heads, d), all of x's dtype and device and contiguous; rope a bool.
+    The tensors must stay alive until the call's kernels have run."""
+    if rel_pos_table is None and q_norm_gamma is None and k_norm_gamma is None and not rope:
+        return None
+    B, C, H, W = x.shape
+    d = C // num_heads
+    for name, t, want in (("rel_pos_table", rel_pos_table, ((2 * H - 1) * (2 * W - 1), num_heads)),
+                          ("q_norm_gamma", q_norm_gamma, (num_heads, d)),
+                          ("k_norm_gamma", k_norm_gamma, (num_heads, d))):
+        if t is None:
+            continue
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+        if t.dtype != x.dtype or t.device != x.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with x's dtype and device")
+    return Options(_ptr(rel_pos_table), _ptr(q_norm_gamma), _ptr(k_norm_gamma), 1 if rope else 0)
+
+
 def forward_into(x, params, num_groups, num_heads, out, workspace, stage=None,
-                 stream=None) -> None:
-    """Enqueue the block (or one stage of it) on `stream` (default: torch's current)."""
+                 stream=None, options=None) -> None:
+    """Enqueue the block (or one stage of it) on `stream` (default: torch's current).
+
+    options: an Options structure (make_options) for ssa_forward_ex, or None."""
     _check_tensors(x, params)
     B, C, H, W = x.shape
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     ptrs = [_ptr(params[k]) for k in PARAM_ORDER]
-    args = (_ptr(x), _ptr(out), ptrs, B, C, H, W, num_groups, num_heads, dtype_code(x.dtype),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), stream.cuda_stream)
-    if stage is None:
-        _raise(ssa_forward(*args), "ssa_forward")
+    head = (_ptr(x), _ptr(out), ptrs, B, C, H, W, num_groups, num_heads, dtype_code(x.dtype))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if stage is not None:
+        if options is not None:
+            raise ValueError("stages run the plain block; options need the whole call")
+        _raise(ssa_forward_stage(STAGES.get(stage, stage), *head, *tail), "ssa_forward_stage")
+    elif options is not None:
+        _raise(ssa_forward_ex(*head, options, *tail), "ssa_forward_ex")
     else:
-        _raise(ssa_forward_stage(STAGES.get(stage, stage), *args), "ssa_forward_stage")
+        _raise(ssa_forward(*head, *tail), "ssa_forward")
 
 
-def spatial_self_attention(x: torch.Tensor, params: dict, num_groups: int,
-                           num_heads: int) -> torch.Tensor:
+def spatial_self_attention(x: torch.Tensor, params: dict, num_groups: int, num_heads: int,
+                           *, rel_pos_table=None, q_norm_gamma=None, k_norm_gamma=None,
+                           rope: bool = False) -> torch.Tensor:
     """out = x + image(MHA(tokens(GN(x)))), shape and dtype of x.
 
     params holds the ten tensors norm_weight, norm_bias (C,), q/k/v/out_weight
-    (C, C) stored (out, in), q/k/v/out_bias (C,), all of x's dtype.
+    (C, C) stored (out, in), q/k/v/out_bias (C,), all of x's dtype; a bias may
+    be None (a projection without a bias).  The keyword options switch on the
+    optional steps of include/ssa.h's ssa_options: a 2-D relative-position
+    bias table, per-head query/key normalisation gammas, rotary embeddings.
     """
     _check_tensors(x, params)
+    opts = make_options(x, num_heads, rel_pos_table, q_norm_gamma, k_norm_gamma, rope)
     out = torch.empty_like(x)
     ws = workspace_for(x, num_groups, num_heads)
-    forward_into(x, params, num_groups, num_heads, out, ws)
+    forward_into(x, params, num_groups, num_heads, out, ws, options=opts)
     return out

@@ -29,7 +29,19 @@ PARAM_ORDER = (
 )
 
 EXPORTS = ("ssa_workspace_size", "ssa_get_workspace_layout", "ssa_forward",
-           "ssa_forward_stage", "ssa_status_string")
+           "ssa_forward_ex", "ssa_forward_stage", "ssa_status_string")
+
+BIAS_KEYS = ("q_bias", "k_bias", "v_bias", "out_bias")
+
+
+class Options(ctypes.Structure):
+    """ssa_options (include/ssa.h)."""
+    _fields_ = [
+        ("rel_pos_table", ctypes.c_void_p),
+        ("q_norm_gamma", ctypes.c_void_p),
+        ("k_norm_gamma", ctypes.c_void_p),
+        ("rope", ctypes.c_int32),
+    ]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -80,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.ssa_forward.argtypes = fwd
     L.ssa_forward_stage.restype = ctypes.c_int
     L.ssa_forward_stage.argtypes = [ctypes.c_int] + fwd
+    L.ssa_forward_ex.restype = ctypes.c_int
+    L.ssa_forward_ex.argtypes = fwd[:19] + [ctypes.POINTER(Options)] + fwd[19:]
     L.ssa_status_string.restype = ctypes.c_char_p
     L.ssa_status_string.argtypes = [ctypes.c_int]
     _lib = L
@@ -121,6 +135,14 @@ def ssa_forward(x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups, num_heads, d
     """Raw call: integer device pointers in, status code out."""
     return int(lib().ssa_forward(x_ptr, out_ptr, *param_ptrs, B, C, H, W, num_groups,
                                  num_heads, int(dtype), ws_ptr, ws_bytes, stream_ptr))
+
+
+def ssa_forward_ex(x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups, num_heads, dtype,
+                   options, ws_ptr, ws_bytes, stream_ptr) -> int:
+    """Raw call with an Options structure (or None: the plain block)."""
+    opt = ctypes.byref(options) if options is not None else None
+    return int(lib().ssa_forward_ex(x_ptr, out_ptr, *param_ptrs, B, C, H, W, num_groups,
+                                    num_heads, int(dtype), opt, ws_ptr, ws_bytes, stream_ptr))
 
 
 def ssa_forward_stage(stage, x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups, num_heads,

@@ -102,30 +102,43 @@ struct Range {
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 ssa_status check_pointers(const Plan& p, const Args& a, size_t ws_bytes) {
-  const void* ptrs[] = {a.x, a.out, a.norm_weight, a.norm_bias, a.w[0], a.w[1], a.w[2], a.w[3],
-                        a.b[0], a.b[1], a.b[2], a.b[3], a.ws};
-  for (const void* q : ptrs)
+  const void* required[] = {a.x, a.out, a.norm_weight, a.norm_bias, a.w[0], a.w[1], a.w[2],
+                            a.w[3], a.ws};
+  for (const void* q : required)
     if (q == nullptr) return SSA_E_NULL;
-  for (const void* q : ptrs)
+  const void* all[] = {a.x, a.out, a.norm_weight, a.norm_bias, a.w[0], a.w[1], a.w[2], a.w[3],
+                       a.b[0], a.b[1], a.b[2], a.b[3], a.ws,
+                       a.rel_pos_table, a.q_norm_gamma, a.k_norm_gamma};
+  for (const void* q : all)  // NULL (an absent optional tensor) is aligned
     if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return SSA_E_ALIGN;
   if (ws_bytes < p.ws.total) return SSA_E_WORKSPACE;
   const size_t e = p.esize;
   const size_t img = size_t(p.B * p.C * p.T) * e;
   auto rng = [](const void* q, size_t bytes) {
     uintptr_t lo = reinterpret_cast<uintptr_t>(q);
-    return Range{lo, lo + bytes};
+    return Range{lo, q == nullptr ? lo : lo + bytes};  // absent: empty range
   };
   Range out = rng(a.out, img);
   Range ws = rng(a.ws, p.ws.total);
+  const size_t table = size_t((2 * p.H - 1) * (2 * p.W - 1) * p.n) * e;
   Range inputs[] = {rng(a.x, img),
                     rng(a.norm_weight, p.C * e), rng(a.norm_bias, p.C * e),
                     rng(a.w[0], p.C * p.C * e), rng(a.w[1], p.C * p.C * e),
                     rng(a.w[2], p.C * p.C * e), rng(a.w[3], p.C * p.C * e),
                     rng(a.b[0], p.C * e), rng(a.b[1], p.C * e),
-                    rng(a.b[2], p.C * e), rng(a.b[3], p.C * e)};
+                    rng(a.b[2], p.C * e), rng(a.b[3], p.C * e),
+                    rng(a.rel_pos_table, table),
+                    rng(a.q_norm_gamma, p.C * e), rng(a.k_norm_gamma, p.C * e)};
   if (overlap(out, ws)) return SSA_E_ALIAS;
   for (const Range& r : inputs)
     if (overlap(out, r) || overlap(ws, r)) return SSA_E_ALIAS;
+  return SSA_OK;
+}
+
+// Rules of the optional steps that depend on the sizes.
+ssa_status check_options(const Plan& p, const Args& a) {
+  if ((a.q_norm_gamma == nullptr) != (a.k_norm_gamma == nullptr)) return SSA_E_CONSTRAINT;
+  if (a.rope && p.d % 2 != 0) return SSA_E_UNSUPPORTED;
   return SSA_OK;
 }
 
@@ -133,7 +146,7 @@ ssa_status run(int first, int last, const void* x, void* out, const void* nw, co
                const void* qw, const void* kw, const void* vw, const void* ow,
                const void* qb, const void* kb, const void* vb, const void* ob,
                int64_t B, int64_t C, int64_t H, int64_t W, int64_t G, int64_t n, int dtype,
-               void* workspace, size_t workspace_bytes, void* stream) {
+               const ssa_options* opt, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   bool empty = false;
   ssa_status st = make_plan(B, C, H, W, G, n, dtype, &p, &empty);
@@ -144,13 +157,22 @@ ssa_status run(int first, int last, const void* x, void* out, const void* nw, co
   a.b[0] = qb; a.b[1] = kb; a.b[2] = vb; a.b[3] = ob;
   a.ws = static_cast<char*>(workspace);
   a.stream = static_cast<hipStream_t>(stream);
+  a.rel_pos_table = opt ? opt->rel_pos_table : nullptr;
+  a.q_norm_gamma = opt ? opt->q_norm_gamma : nullptr;
+  a.k_norm_gamma = opt ? opt->k_norm_gamma : nullptr;
+  a.rope = opt != nullptr && opt->rope != 0;
+  st = check_options(p, a);
+  if (st != SSA_OK) return st;
   st = check_pointers(p, a, workspace_bytes);
   if (st != SSA_OK) return st;
   for (int s = first; s <= last; ++s) {
     hipError_t e = hipSuccess;
     switch (s) {
       case SSA_STAGE_GN_STATS: e = launch_gn_stats(p, a); break;
-      case SSA_STAGE_QKV: e = launch_qkv_proj(p, a); break;
+      case SSA_STAGE_QKV:
+        e = launch_qkv_proj(p, a);
+        if (e == hipSuccess && (a.rope || a.q_norm_gamma != nullptr)) e = launch_qk_post(p, a);
+        break;
       case SSA_STAGE_ATTENTION: e = launch_attention(p, a); break;
       case SSA_STAGE_OUT_PROJ: e = launch_out_proj(p, a); break;
     }
@@ -193,7 +215,21 @@ ssa_status ssa_forward(const void* x, void* out, const void* norm_weight, const 
                        void* workspace, size_t workspace_bytes, void* stream) {
   return ssa::run(SSA_STAGE_GN_STATS, SSA_STAGE_OUT_PROJ, x, out, norm_weight, norm_bias,
                   q_weight, k_weight, v_weight, out_weight, q_bias, k_bias, v_bias, out_bias,
-                  B, C, H, W, num_groups, num_heads, dtype, workspace, workspace_bytes, stream);
+                  B, C, H, W, num_groups, num_heads, dtype, nullptr, workspace, workspace_bytes,
+                  stream);
+}
+
+ssa_status ssa_forward_ex(const void* x, void* out, const void* norm_weight,
+                          const void* norm_bias, const void* q_weight, const void* k_weight,
+                          const void* v_weight, const void* out_weight, const void* q_bias,
+                          const void* k_bias, const void* v_bias, const void* out_bias,
+                          int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
+                          int64_t num_heads, int dtype, const ssa_options* options,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return ssa::run(SSA_STAGE_GN_STATS, SSA_STAGE_OUT_PROJ, x, out, norm_weight, norm_bias,
+                  q_weight, k_weight, v_weight, out_weight, q_bias, k_bias, v_bias, out_bias,
+                  B, C, H, W, num_groups, num_heads, dtype, options, workspace, workspace_bytes,
+                  stream);
 }
 
 ssa_status ssa_forward_stage(int stage, const void* x, void* out, const void* norm_weight,
@@ -206,19 +242,21 @@ ssa_status ssa_forward_stage(int stage, const void* x, void* out, const void* no
   if (stage < SSA_STAGE_GN_STATS || stage > SSA_STAGE_OUT_PROJ) return SSA_E_STAGE;
   return ssa::run(stage, stage, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight,
                   out_weight, q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups,
-                  num_heads, dtype, workspace, workspace_bytes, stream);
+                  num_heads, dtype, nullptr, workspace, workspace_bytes, stream);
 }
 
 const char* ssa_status_string(int status) {
   switch (status) {
     case SSA_OK: return "ok";
-    case SSA_E_NULL: return "a required pointer is NULL";
+    case SSA_E_NULL: return "a required pointer is NULL (only the biases may be NULL)";
     case SSA_E_SHAPE: return "invalid shape: sizes must be >= 0 and C >= 1";
-    case SSA_E_CONSTRAINT: return "num_groups and num_heads must be >= 1 and divide C";
+    case SSA_E_CONSTRAINT:
+      return "num_groups and num_heads must be >= 1 and divide C; query and key norm gammas "
+             "come together";
     case SSA_E_DTYPE: return "unknown dtype";
     case SSA_E_UNSUPPORTED:
-      return "unsupported size: head size must be 1..128 (fp32) or 32/64/96/128 (bf16), "
-             "and each tensor below 2^31 elements";
+      return "unsupported size: head size must be 1..128 (fp32) or 32/64/96/128 (bf16), even "
+             "with rotary embeddings, and each tensor below 2^31 elements";
     case SSA_E_WORKSPACE: return "workspace smaller than ssa_workspace_size()";
     case SSA_E_ALIAS: return "out or workspace overlaps another buffer";
     case SSA_E_ALIGN: return "a pointer is not 16-byte aligned";

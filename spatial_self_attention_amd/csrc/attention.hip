@@ -51,7 +51,9 @@ struct AttnParams {
   void* o;         // (B, T, C)
   int T, Tp, n, d, C;
   int qtiles;      // query tiles per (b, head)
-  float scale;     // log2(e) / sqrt(d)
+  float scale;     // log2(e) / sqrt(d) (fp32 path; log2(e) with query/key normalisation)
+  const void* rel; // ((2H-1)(2W-1), n) relative-position table, or NULL
+  int H, W;
 };
 
 // ---------------------------------------------------------------------------
@@ -254,10 +256,48 @@ __device__ __forceinline__ float probs(bf16x8 (&pb)[2], const f32x16& s, float d
 // FIRST: the first sub-block, which sets m.  Returns whether m was raised
 // (wave-uniform), with the raise per query block in delta; O is rescaled
 // after the P V products already issued for earlier sub-blocks.
-template <int D, int QB, int KT, bool MASK>
+// Relative-position bias of one wave's queries (HNDL attention operator,
+// "Relative position bias"): column `head` of the table (stride n), and the
+// grid row / column of each of the wave's query blocks' lane query.
+template <int QB>
+struct RelPos {
+  const bf16* tab;   // table + head
+  int H, W, n;
+  int qr[QB], qc[QB];
+};
+
+// Adds log2(e) * table[(row(q)-row(k)+H-1)(2W-1) + col(q)-col(k)+W-1, head]
+// to the scores of one 32-key sub-block (keys >= T are left alone: masked).
+template <int QB>
+__device__ __forceinline__ void add_rel(f32x16 (&s)[QB], const RelPos<QB>& rp, int kfirst, int T,
+                                        int half) {
+#pragma unroll
+  for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
+    const int k0 = kfirst + 8 * run + 4 * half;
+    int kr = k0 / rp.W, kc = k0 - kr * rp.W;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (k0 + e < T) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int idx = (rp.qr[qb] - kr + rp.H - 1) * (2 * rp.W - 1) + (rp.qc[qb] - kc + rp.W - 1);
+          s[qb][4 * run + e] += kLog2e * static_cast<float>(rp.tab[int64_t(idx) * rp.n]);
+        }
+      }
+      if (++kc == rp.W) {
+        kc = 0;
+        ++kr;
+      }
+    }
+  }
+}
+
+template <int D, int QB, int KT, bool MASK, bool REL>
 __device__ __forceinline__ bool softmax_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
                                               bf16x8 (&pb)[QB][2], float (&delta)[QB], int kb,
-                                              int kbase, int T, int half, bool first) {
+                                              int kbase, int T, int half, bool first,
+                                              const RelPos<QB>& rp) {
+  if constexpr (REL) add_rel<QB>(s, rp, kbase + kb * 32, T, half);
   if constexpr (MASK) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -311,9 +351,10 @@ __device__ __forceinline__ bool softmax_block(AttnState<D, QB>& st, f32x16 (&s)[
 // fragments those MFMAs need were read during step kb-1, and step kb reads
 // the fragments of step kb+1 (K of kb+2, V of kb).  When the softmax raises
 // m, the scores of kb+1 (formed against the old m) are shifted by the raise.
-template <int D, int QB, int KT, bool MASK>
+template <int D, int QB, int KT, bool MASK, bool REL>
 __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* buf, int k0,
-                                            int T, int half, int col, bool first) {
+                                            int T, int half, int col, bool first,
+                                            const RelPos<QB>& rp) {
   typedef Tile<D, QB, KT> TL;
   constexpr int NKB = TL::NKB;
   const bf16* Ks = buf;
@@ -330,7 +371,8 @@ __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* bu
       VFrag<D> vf;
       read_k<D, QB, KT>(kf, Ks, kb, half, col);
       qk_mfma<D, QB>(s[0], st, kf);
-      softmax_block<D, QB, KT, true>(st, s[0], pb[0], delta, kb, k0, T, half, first && kb == 0);
+      softmax_block<D, QB, KT, true, REL>(st, s[0], pb[0], delta, kb, k0, T, half,
+                                          first && kb == 0, rp);
       read_v<D, QB, KT>(vf, Vs, kb, half, col);
       pv_mfma<D, QB>(st, pb[0], vf);
     }
@@ -357,8 +399,8 @@ __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* bu
     }
     if (kb + 1 < NKB) qk_mfma<D, QB>(s[(kb + 1) & 1], st, kf[(kb + 1) & 1]);
     if (kb > 0) pv_mfma<D, QB>(st, pb[(kb - 1) & 1], vf[(kb - 1) & 1]);
-    const bool raised = softmax_block<D, QB, KT, MASK>(st, s[kb & 1], pb[kb & 1], delta, kb, k0, T,
-                                                       half, first && kb == 0);
+    const bool raised = softmax_block<D, QB, KT, MASK, REL>(st, s[kb & 1], pb[kb & 1], delta, kb,
+                                                            k0, T, half, first && kb == 0, rp);
     if (kb + 1 < NKB && raised) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -425,8 +467,9 @@ constexpr int attn_min_blocks() { return D <= 64 ? 3 : 2; }
 // NW = 4: 128 queries per work-group, several work-groups per CU.  NW = 8:
 // 256 queries per work-group, used for short sequences (T <= 256, one
 // work-group per (sample, head)) so that K and V are read once per head.
-template <int D, int QB, int KT, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? attn_min_blocks<D>() : 1) void attn_bf16_kernel(AttnParams ap) {
+// (The relative-position variant needs a few more registers: two work-groups per CU.)
+template <int D, int QB, int KT, int NW, bool REL>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? (REL ? 2 : attn_min_blocks<D>()) : 1) void attn_bf16_kernel(AttnParams ap) {
   typedef Tile<D, QB, KT, NW> TL;
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF];
 
@@ -445,6 +488,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? attn_min_blocks<D>() : 1) void a
 
   AttnState<D, QB> st;
   init_state<D, QB>(st, Q, qtile * TL::QT + wave * TL::QPW, T, half, col);
+  RelPos<QB> rp;
+  if constexpr (REL) {
+    rp.tab = static_cast<const bf16*>(ap.rel) + head;
+    rp.H = ap.H;
+    rp.W = ap.W;
+    rp.n = ap.n;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {  // rows past T take the last query's place
+      const int qi = min(qtile * TL::QT + wave * TL::QPW + qb * 32 + col, T - 1);
+      rp.qr[qb] = qi / ap.W;
+      rp.qc[qb] = qi - rp.qr[qb] * ap.W;
+    }
+  }
 
   const int ntiles = (T + KT - 1) / KT;
   const int nfull = T / KT;
@@ -462,13 +518,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? attn_min_blocks<D>() : 1) void a
       load_tile<D, QB, KT, NW, false>(pf, K, Vt, ap.Tp, kn, T, tid);
     else if (j + 1 < ntiles)
       load_tile<D, QB, KT, NW, true>(pf, K, Vt, ap.Tp, kn, T, tid);
-    attend_tile<D, QB, KT, false>(st, lds + (j & 1) * TL::BUF, j * KT, T, half, col, j == 0);
+    attend_tile<D, QB, KT, false, REL>(st, lds + (j & 1) * TL::BUF, j * KT, T, half, col, j == 0,
+                                       rp);
     if (j + 1 < ntiles) store_tile<D, QB, KT, NW>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
   }
   if (nfull < ntiles) {  // the partial last tile
     __syncthreads();
-    attend_tile<D, QB, KT, true>(st, lds + (nfull & 1) * TL::BUF, nfull * KT, T, half, col,
-                                 nfull == 0);
+    attend_tile<D, QB, KT, true, REL>(st, lds + (nfull & 1) * TL::BUF, nfull * KT, T, half, col,
+                                      nfull == 0, rp);
   }
 
   write_o<D, QB>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col);
@@ -479,7 +536,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? attn_min_blocks<D>() : 1) void a
 // ---------------------------------------------------------------------------
 constexpr int FQT = 64, FKT = 32;
 
-template <int DP>  // d rounded up to a supported width; each lane owns DP/4 dims
+template <int DP, bool REL>  // d rounded up to a supported width; each lane owns DP/4 dims
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
   constexpr int NPT = DP / 4;
   __shared__ float Ks[FKT * (DP + 1)];
@@ -504,6 +561,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
   }
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = ap.scale;
+  // relative-position bias: this lane's query row / column (rows past T
+  // take the last query's place)
+  const float* rtab = REL ? static_cast<const float*>(ap.rel) + head : nullptr;
+  const int qc_ = min(qi, T - 1);
+  const int qrow = REL ? qc_ / ap.W : 0, qcol = REL ? qc_ - qrow * ap.W : 0;
 
   for (int k0 = 0; k0 < T; k0 += FKT) {
     __syncthreads();
@@ -527,7 +589,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
       for (int i = 0; i < NPT; ++i) part += qv[i] * Ks[j * (DP + 1) + i * 4 + sub];
       part += __shfl_xor(part, 1, 64);
       part += __shfl_xor(part, 2, 64);
-      s[j] = (k0 + j < T) ? part * sc : -INFINITY;
+      float rel = 0.f;
+      if (REL && k0 + j < T) {
+        const int kr = (k0 + j) / ap.W, kc = (k0 + j) - kr * ap.W;
+        rel = kLog2e * rtab[int64_t((qrow - kr + ap.H - 1) * (2 * ap.W - 1) + (qcol - kc + ap.W - 1)) * ap.n];
+      }
+      s[j] = (k0 + j < T) ? part * sc + rel : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -555,11 +622,20 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
   }
 }
 
-template <int D, int QB, int KT, int NW>
-void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
+template <int D, int QB, int KT, int NW, bool REL>
+void launch_bf16_v(AttnParams ap, int64_t bh, hipStream_t stream) {
   typedef Tile<D, QB, KT, NW> TL;
   ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
-  attn_bf16_kernel<D, QB, KT, NW><<<dim3(unsigned(bh * ap.qtiles)), TL::NTHR, 0, stream>>>(ap);
+  attn_bf16_kernel<D, QB, KT, NW, REL><<<dim3(unsigned(bh * ap.qtiles)), TL::NTHR, 0, stream>>>(ap);
+}
+
+// The relative-position variant comes in the 4-wave shape only.
+template <int D, int QB, int KT, int NW>
+void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
+  if (ap.rel != nullptr)
+    launch_bf16_v<D, QB, KT, 4, true>(ap, bh, stream);
+  else
+    launch_bf16_v<D, QB, KT, NW, false>(ap, bh, stream);
 }
 
 }  // namespace
@@ -575,7 +651,12 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   ap.n = int(p.n);
   ap.d = int(p.d);
   ap.C = int(p.C);
-  ap.scale = kLog2e / sqrtf(float(p.d));
+  // normalised queries and keys are not divided by sqrt(d) (bf16 folds the
+  // scale into the stored queries instead)
+  ap.scale = a.q_norm_gamma != nullptr ? kLog2e : kLog2e / sqrtf(float(p.d));
+  ap.rel = a.rel_pos_table;
+  ap.H = int(p.H);
+  ap.W = int(p.W);
   const int64_t bh = p.B * p.n;
   if (p.dtype == SSA_BF16) {
     // one 256-query work-group per head when the heads alone fill the chip
@@ -595,12 +676,16 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   } else {
     ap.qtiles = int((p.T + FQT - 1) / FQT);
     dim3 grid(unsigned(bh * ap.qtiles));
+    const bool rel = ap.rel != nullptr;
     if (p.d <= 32)
-      attn_f32_kernel<32><<<grid, 256, 0, a.stream>>>(ap);
+      rel ? attn_f32_kernel<32, true><<<grid, 256, 0, a.stream>>>(ap)
+          : attn_f32_kernel<32, false><<<grid, 256, 0, a.stream>>>(ap);
     else if (p.d <= 64)
-      attn_f32_kernel<64><<<grid, 256, 0, a.stream>>>(ap);
+      rel ? attn_f32_kernel<64, true><<<grid, 256, 0, a.stream>>>(ap)
+          : attn_f32_kernel<64, false><<<grid, 256, 0, a.stream>>>(ap);
     else
-      attn_f32_kernel<128><<<grid, 256, 0, a.stream>>>(ap);
+      rel ? attn_f32_kernel<128, true><<<grid, 256, 0, a.stream>>>(ap)
+          : attn_f32_kernel<128, false><<<grid, 256, 0, a.stream>>>(ap);
   }
   return hipGetLastError();
 }

@@ -207,10 +207,11 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
         if (m >= pp.M) continue;
         const int which = MODE == kQkv ? m / C : 0;
         const int c = m - which * C;
-        const bf16* bias = static_cast<const bf16*>(pp.bias[which]);
+        const bf16* bias = static_cast<const bf16*>(pp.bias[which]);  // NULL: no bias
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + static_cast<float>(bias[c + e]);
+        for (int e = 0; e < 4; ++e)
+          v[e] = acc[i][j][4 * g + e] + (bias ? static_cast<float>(bias[c + e]) : 0.f);
         if constexpr (MODE == kQkv) {
           const int head = c / pp.d, dd = c - head * pp.d;
           const int64_t bh = b * pp.n + head;
@@ -487,7 +488,8 @@ __device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const ProjP
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int cl = i * 32 + col;
-      const float bias = static_cast<float>(static_cast<const bf16*>(pp.bias[0])[ec.mw + cl]);
+      const bf16* bp = static_cast<const bf16*>(pp.bias[0]);  // NULL: no bias
+      const float bias = bp ? static_cast<float>(bp[ec.mw + cl]) : 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -500,11 +502,11 @@ __device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const ProjP
     }
   } else if constexpr (TR) {  // V
     bf16* E = lds + wave * 64 * EPB;
-    const bf16* bias = static_cast<const bf16*>(pp.bias[2]) + (ec.mw - 2 * C);
+    const bf16* bias = static_cast<const bf16*>(pp.bias[2]);  // NULL: no bias
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int cl = i * 32 + col;
-      const float bv = static_cast<float>(bias[cl]);
+      const float bv = bias ? static_cast<float>(bias[ec.mw - 2 * C + cl]) : 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -519,13 +521,14 @@ __device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const ProjP
     bf16* E = lds + wave * 64 * EPB;
     const int which = ec.mw / C;
     const float sc = which == 0 ? pp.q_scale : 1.f;
-    const bf16* bias = static_cast<const bf16*>(pp.bias[which]) + (ec.mw - which * C);
+    const bf16* bias = static_cast<const bf16*>(pp.bias[which]);  // NULL: no bias
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int cl = i * 32 + 8 * g + 4 * half;
-        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(bias + cl);
+        const bf16x4 bv = bias ? *reinterpret_cast<const bf16x4*>(bias + (ec.mw - which * C) + cl)
+                               : bf16x4{};
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           bf16x4 pk;
@@ -710,7 +713,8 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjParams pp) {
     if (m >= pp.M) continue;
     const int which = MODE == kQkv ? m / C : 0;
     const int c = m - which * C;
-    const float bias = static_cast<const float*>(pp.bias[which])[c];
+    const float* bp = static_cast<const float*>(pp.bias[which]);  // NULL: no bias
+    const float bias = bp ? bp[c] : 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t nn = n0 + tx * 4 + j;

@@ -50,10 +50,19 @@ struct Args {
   const void* norm_weight;
   const void* norm_bias;
   const void* w[4];  // q, k, v, out weights
-  const void* b[4];  // q, k, v, out biases
+  const void* b[4];  // q, k, v, out biases (NULL: no bias)
   char* ws;
   hipStream_t stream;
+  // optional steps (ssa_options); NULL / false when off
+  const void* rel_pos_table;
+  const void* q_norm_gamma;
+  const void* k_norm_gamma;
+  bool rope;
 };
+
+// In-place query/key normalisation and rotary embedding of the workspace Q
+// and K (run inside the QKV stage when either option is on).
+hipError_t launch_qk_post(const Plan& p, const Args& a);
 
 // Launchers (one per stage); each returns hipSuccess or the launch error.
 hipError_t launch_gn_stats(const Plan& p, const Args& a);

@@ -121,6 +121,41 @@ def draw(wl: Workload, seed: int, stress: bool = False):
 
 
 def to_f64(x: torch.Tensor, params: dict):
-    """Lossless upcast of the drawn tensors to fp64 numpy arrays (for the oracle)."""
+    """Lossless upcast of the drawn tensors to fp64 numpy arrays (for the oracle).
+
+    A None parameter (a projection without a bias) stays None."""
     return (x.to(torch.float64).numpy(),
-            {k: v.to(torch.float64).numpy() for k, v in params.items()})
+            {k: (None if v is None else v.to(torch.float64).numpy()) for k, v in params.items()})
+
+
+def draw_options(wl: Workload, seed: int, rel_pos: bool = False, qk_norm: bool = False,
+                 rope: bool = False, stress: bool = False) -> dict:
+    """Tensors of the optional steps, as CPU torch tensors in the workload dtype.
+
+    rel_pos_table ((2H-1)(2W-1), n) ~ N(0, 1): logit shifts of order one, so
+    the bias moves the attention visibly.  q/k norm gammas (n, d) ~
+    U(0.5, 1.5) / sqrt(d) around the 1/sqrt(d) the qk-norm page starts from
+    (normalised scores of order one); stress multiplies them by 3 (peaked
+    attention).  Keys: rel_pos_table, q_norm_gamma, k_norm_gamma, rope; absent
+    steps are None / False.
+    """
+    rng = np.random.default_rng(seed + 7919)
+    H, W, n, d = wl.H, wl.W, wl.num_heads, wl.d
+    dt = wl.torch_dtype
+    out = {"rel_pos_table": None, "q_norm_gamma": None, "k_norm_gamma": None, "rope": rope}
+    if rel_pos:
+        t = rng.standard_normal(((2 * H - 1) * (2 * W - 1), n))
+        out["rel_pos_table"] = torch.from_numpy(t).to(dt).contiguous()
+    if qk_norm:
+        g = 3.0 if stress else 1.0
+        for k in ("q_norm_gamma", "k_norm_gamma"):
+            v = g * rng.uniform(0.5, 1.5, size=(n, d)) / np.sqrt(d)
+            out[k] = torch.from_numpy(v).to(dt).contiguous()
+    return out
+
+
+def options_f64(opts: dict) -> dict:
+    """The oracle's keyword arguments for draw_options' tensors (fp64, lossless)."""
+    f = lambda t: None if t is None else t.to(torch.float64).numpy()
+    return {"rel_pos_table": f(opts["rel_pos_table"]), "q_norm_gamma": f(opts["q_norm_gamma"]),
+            "k_norm_gamma": f(opts["k_norm_gamma"]), "rope_on": bool(opts["rope"])}

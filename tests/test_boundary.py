@@ -133,7 +133,14 @@ OK_SHAPE = (2, 64, 4, 4, 8, 2, ssa.SSA_BF16)
      "SSA_E_UNSUPPORTED"),
     ("null x", dict(shape=OK_SHAPE, ptr={"x": 0}), "SSA_E_NULL"),
     ("null out", dict(shape=OK_SHAPE, ptr={"out": 0}), "SSA_E_NULL"),
-    ("null v_bias", dict(shape=OK_SHAPE, ptr={"v_bias": 0}), "SSA_E_NULL"),
+    # biases are nullable: a NULL bias passes the pointer checks and the call
+    # stops at the next rule (a too-small workspace here, so nothing launches)
+    ("null v_bias accepted", dict(shape=OK_SHAPE, ptr={"v_bias": 0}, ws_bytes=1024),
+     "SSA_E_WORKSPACE"),
+    ("all biases null accepted", dict(shape=OK_SHAPE, ptr={"q_bias": 0, "k_bias": 0, "v_bias": 0,
+                                                           "out_bias": 0}, ws_bytes=1024),
+     "SSA_E_WORKSPACE"),
+    ("null norm_weight", dict(shape=OK_SHAPE, ptr={"norm_weight": 0}), "SSA_E_NULL"),
     ("null workspace", dict(shape=OK_SHAPE, ptr={"ws": 0}), "SSA_E_NULL"),
     ("misaligned x", dict(shape=OK_SHAPE, ptr={"x": (1 << 50) + 8}), "SSA_E_ALIGN"),
     ("misaligned weight", dict(shape=OK_SHAPE, ptr={"k_weight": (1 << 50) + 2}), "SSA_E_ALIGN"),
@@ -188,3 +195,46 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "libssa.so"))
     with pytest.raises(RuntimeError, match="not built"):
         bnd.lib()
+
+
+# ---------------------------------------------------------------------------
+# ssa_forward_ex: the optional steps' rules, all checked before any launch
+# ---------------------------------------------------------------------------
+
+def call_ex(shape, opt, ptr=None, ws_bytes=None):
+    B, C, H, W, G, n, dt = shape
+    fake = Fake()
+    p = {k: fake() for k in ["x", "out", "ws"] + list(bnd.PARAM_ORDER)}
+    p.update(ptr or {})
+    if ws_bytes is None:
+        ws_bytes = ssa.ssa_workspace_size(B, C, H, W, G, n, dt) or 1 << 20
+    params = [p[k] for k in bnd.PARAM_ORDER]
+    return bnd.STATUS_NAMES[ssa.ssa_forward_ex(p["x"], p["out"], params, B, C, H, W, G, n, dt,
+                                               opt, p["ws"], ws_bytes, 0)]
+
+
+def test_ex_query_key_gammas_come_together():
+    assert call_ex(OK_SHAPE, bnd.Options(0, 1 << 50, 0, 0)) == "SSA_E_CONSTRAINT"
+    assert call_ex(OK_SHAPE, bnd.Options(0, 0, 1 << 50, 0)) == "SSA_E_CONSTRAINT"
+
+
+def test_ex_rope_needs_even_head():
+    assert call_ex((2, 6, 4, 4, 3, 2, ssa.SSA_F32), bnd.Options(0, 0, 0, 1)) == "SSA_E_UNSUPPORTED"
+
+
+def test_ex_misaligned_option_tensor():
+    assert call_ex(OK_SHAPE, bnd.Options((1 << 50) + 2, 0, 0, 0)) == "SSA_E_ALIGN"
+    assert call_ex(OK_SHAPE, bnd.Options(0, (1 << 50) + 4, (1 << 51), 0)) == "SSA_E_ALIGN"
+
+
+def test_ex_option_tensor_must_not_alias_out_or_workspace():
+    t = 1 << 50
+    # the table of OK_SHAPE is (7*7, 2) bf16 = 196 bytes: out starting inside it overlaps
+    assert call_ex(OK_SHAPE, bnd.Options(t, 0, 0, 0), ptr={"out": t + 64}) == "SSA_E_ALIAS"
+    assert call_ex(OK_SHAPE, bnd.Options(0, t, t + (1 << 30), 0), ptr={"ws": t + 64}) == "SSA_E_ALIAS"
+
+
+def test_ex_valid_options_reach_the_workspace_check():
+    opt = bnd.Options(1 << 50, 1 << 51, (1 << 51) + (1 << 30), 1)
+    assert call_ex(OK_SHAPE, opt, ws_bytes=1024) == "SSA_E_WORKSPACE"
+    assert call_ex(OK_SHAPE, None, ws_bytes=1024) == "SSA_E_WORKSPACE"

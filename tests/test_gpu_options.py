@@ -1,0 +1,130 @@
+"""GPU parity of the optional steps (ssa_forward_ex, nullable biases) against
+the fp64 oracle, through the C ABI.
+
+The steps: projections without a bias (HNDL attention operator, qkv_bias /
+out_bias), per-head query/key normalisation (vit-pytorch qk-norm, RMSNorm),
+rotary embeddings and the 2-D relative-position bias (HNDL attention
+operator).  Tolerances as for the plain block: fp32 max |gpu - oracle| <= 1e-4,
+bf16 normwise max-relative <= 2e-2; every bf16 case also runs on stressed
+inputs (q/k weights x4, x x0.05, tripled norm gammas).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as ORA
+import spatial_self_attention_amd as ssa
+from spatial_self_attention_amd.inputs import (WORKLOADS, Workload, draw, draw_options, options_f64,
+                                               to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def err(got, want, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    e = float(np.max(np.abs(got - want)))
+    if dtype == "bf16":
+        e /= max(float(np.max(np.abs(want))), 1e-30)
+    return e
+
+
+def run_case(wl, seed, stress, drop_bias=(), **opt_flags):
+    x, p = draw(wl, seed, stress=stress)
+    for k in drop_bias:
+        p[k] = None
+    opts = draw_options(wl, seed, stress=stress, **opt_flags)
+    print(f"[gpu] {wl.name} dtype={wl.dtype} B={wl.B} C={wl.C} H={wl.H} W={wl.W} "
+          f"n={wl.num_heads} seed={seed} stress={stress} drop={drop_bias} opts={opt_flags}",
+          flush=True)
+    dev = lambda t: None if t is None else t.to(DEV)
+    out = ssa.spatial_self_attention(
+        x.to(DEV), {k: dev(v) for k, v in p.items()}, wl.num_groups, wl.num_heads,
+        rel_pos_table=dev(opts["rel_pos_table"]), q_norm_gamma=dev(opts["q_norm_gamma"]),
+        k_norm_gamma=dev(opts["k_norm_gamma"]), rope=opts["rope"])
+    torch.cuda.synchronize()
+    return x, p, opts, out
+
+
+BIAS_CASES = [
+    (WORKLOADS[0], ("q_bias", "k_bias", "v_bias")),
+    (WORKLOADS[0], ("out_bias",)),
+    (WORKLOADS[2].replace(B=2), ("q_bias", "k_bias", "v_bias", "out_bias")),
+    (WORKLOADS[3].replace(B=1, H=20, W=21), ("k_bias", "out_bias")),
+    (Workload("5x7 bf16", "bf16", 2, 128, 5, 7, 4, 2), ("v_bias",)),
+]
+
+
+@pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
+@pytest.mark.parametrize("case", BIAS_CASES, ids=lambda c: f"{c[0].name}-{'+'.join(c[1])}")
+def test_nullable_biases(case, stress):
+    wl, drop = case
+    x, p, _, out = run_case(wl, 41, stress, drop_bias=drop)
+    want = ORA.forward(*to_f64(x, p), wl.num_groups, wl.num_heads)
+    e = err(out.double().cpu().numpy(), want, wl.dtype)
+    print(f"  err {e:.3e}", flush=True)
+    assert e <= TOL[wl.dtype]
+
+
+OPT_SHAPES = [
+    WORKLOADS[0],                                              # fp32 d32 8x8
+    Workload("fp32 d=50 7x9", "f32", 2, 100, 7, 9, 4, 2),
+    WORKLOADS[1].replace(B=2),                                 # bf16 d128 14x14
+    WORKLOADS[2].replace(B=2),                                 # bf16 d64 16x16
+    WORKLOADS[3].replace(B=1, H=24, W=29),                     # bf16 d64, several key tiles, ragged
+    Workload("bf16 d32 9x11", "bf16", 2, 64, 9, 11, 8, 2),
+    Workload("bf16 d96 6x13", "bf16", 1, 192, 6, 13, 6, 2),
+]
+OPT_FLAGS = {
+    "relpos": dict(rel_pos=True),
+    "rope": dict(rope=True),
+    "qknorm": dict(qk_norm=True),
+    "all": dict(rel_pos=True, rope=True, qk_norm=True),
+}
+
+
+@pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
+@pytest.mark.parametrize("flags", sorted(OPT_FLAGS))
+@pytest.mark.parametrize("wl", OPT_SHAPES, ids=lambda w: f"{w.name}-{w.dtype}")
+def test_options(wl, flags, stress):
+    x, p, opts, out = run_case(wl, 51, stress, **OPT_FLAGS[flags])
+    want = ORA.forward(*to_f64(x, p), wl.num_groups, wl.num_heads, **options_f64(opts))
+    e = err(out.double().cpu().numpy(), want, wl.dtype)
+    print(f"  err {e:.3e}", flush=True)
+    assert e <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_options_full_size_sampled(idx):
+    wl = WORKLOADS[idx]
+    x, p, opts, out = run_case(wl, 1000 + idx, False, drop_bias=("k_bias",),
+                               rel_pos=True, rope=True, qk_norm=True)
+    x64, p64 = to_f64(x, p)
+    og = out.double().cpu().numpy().reshape(wl.B, wl.C, wl.T)
+    assert np.isfinite(og).all()
+    rng = np.random.default_rng(idx)
+    worst = 0.0
+    for b in sorted({0, wl.B - 1}):
+        rows = np.unique(np.concatenate([[0, wl.T - 1], rng.integers(0, wl.T, 6)]))
+        want = ORA.forward_pixels(x64, p64, wl.num_groups, wl.num_heads, b, rows, **options_f64(opts))
+        e = float(np.max(np.abs(og[b][:, rows] - want))) / float(np.max(np.abs(want)))
+        worst = max(worst, e)
+    print(f"  sampled err {worst:.3e}", flush=True)
+    assert worst <= TOL[wl.dtype]
+
+
+def test_options_off_equals_plain_call():
+    """ssa_forward_ex with no option set is ssa_forward, bit for bit."""
+    wl = WORKLOADS[3].replace(B=1, H=16, W=20)
+    x, p = draw(wl, 61)
+    xg = x.to(DEV)
+    pg = {k: v.to(DEV) for k, v in p.items()}
+    ref = ssa.spatial_self_attention(xg, pg, wl.num_groups, wl.num_heads)
+    out = torch.empty_like(xg)
+    ws = ssa.workspace_for(xg, wl.num_groups, wl.num_heads)
+    ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws, options=ssa.Options(0, 0, 0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
