@@ -60,7 +60,7 @@ def stage_work(wl):
 
 # Kernel names (as rocprofv3 prints them) behind each stage, for the counters.
 STAGE_KERNELS = {
-    "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
+    "gn_stats": "gn_stats_kernel (+ gn_finalize_kernel when segments are split)",
     "qkv": "gemm_bf16_kernel<0>",
     "attention": "attn_bf16_kernel",
     "out_proj": "gemm_bf16_kernel<1>",
