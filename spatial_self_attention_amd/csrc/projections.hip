@@ -246,10 +246,12 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernels, main path (C % 64 == 0 and T % 4 == 0)
 //
-// 128 x 128 x 64 work-group tiles, double-buffered in LDS: the next k-step is
-// fetched into registers (and for Q/K/V normalised) while the current one
-// feeds the MFMAs, then written to the other buffer; one barrier per k-step.
-// Each wave owns a 64 x 64 quadrant as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.
+// 128 x 128 x 64 work-group tiles, two LDS buffers and two register stages:
+// the loads of a k-step go out two steps ahead, and a step is written to LDS
+// (for Q/K/V normalised) part by part between the MFMAs of the step before;
+// one barrier per k-step.  The epilogue's loads (bias, residual) go out before
+// the last two steps.  Each wave owns a 64 x 64 quadrant as 2 x 2
+// v_mfma_f32_32x32x16_bf16 blocks.
 // The orientation of a wave's product follows its store layout:
 //  * Q and K (token-major): D = W Z^T, a lane holds 4 consecutive channels of
 //    one token -> 8-byte stores into (B, n, T, d);
@@ -284,9 +286,9 @@ __device__ __forceinline__ int xcd_remap_gemm(int w, int nwg) {
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // One k-step of A (weight rows) and B in registers, as loaded: for the QKV
-// projection B is raw x (8 channel rows x 4 tokens) plus the 8 (a, s) GN
-// coefficients of those channels, normalised only when written to LDS so that
-// the loads stay in flight behind the current step's MFMAs.
+// projection B is raw x (8 channel rows x 4 tokens) and the (a, s) GN
+// coefficients of those 8 channels, normalised only when written to LDS, so
+// that the loads stay in flight behind the MFMAs of the step before.
 struct Stage {
   bf16x8 a[4];
   bf16x8 b[4];     // kOut: 4 token rows of O
@@ -365,105 +367,68 @@ __device__ __forceinline__ void gemm_load(Stage& sg, const LoadCtx& lc, int k0) 
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      sg.cf[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lc.rc, lc.vc + 16 * q, k0 * 8, 0));
-    const int sx = k0 * lc.xrow;  // k0 channel rows further down
+      sg.cf[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lc.rc, lc.vc, k0 * 8 + 16 * q, 0));
+    // channel row k0 + j: the row step goes into the scalar offset, so one
+    // per-thread offset serves all eight loads
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      sg.xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(lc.rb, lc.vx + j * lc.xrow, sx, 0));
+      sg.xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(lc.rb, lc.vx, (k0 + j) * lc.xrow, 0));
+  }
+}
+
+// Part u (0..3) of writing a register stage to LDS: A vector u (row
+// (tid >> 3) + 32u) and, for the output projection, B vector u (token row
+// (tid >> 3) + 32u of O); for Q/K/V token tq*4 + u of the thread's quad,
+// normalised: GN(x) = a x + s in fp32, rounded once to bf16, 8 channels.
+template <int MODE>
+__device__ __forceinline__ void store_part(bf16* As, bf16* Bs, const Stage& sg, int tid, int u) {
+  const int v = tid + 256 * u;
+  *reinterpret_cast<bf16x8*>(&As[(v >> 3) * GP + (v & 7) * 8]) = sg.a[u];
+  if constexpr (MODE == kOut) {
+    *reinterpret_cast<bf16x8*>(&Bs[(v >> 3) * GP + (v & 7) * 8]) = sg.b[u];
+  } else {
+    bf16x8 z;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = sg.cf[j >> 1][(j & 1) * 2], sh = sg.cf[j >> 1][(j & 1) * 2 + 1];
+      const unsigned w = sg.xr[j][u >> 1];  // tokens 2(u>>1), 2(u>>1)+1 of the quad
+      const float xv = __uint_as_float((u & 1) ? (w & 0xffff0000u) : (w << 16));
+      z[j] = static_cast<bf16>(fmaf(a, xv, sh));
+    }
+    const int tq = qkv_tq(tid), co = qkv_co(tid);
+    *reinterpret_cast<bf16x8*>(&Bs[(tq * 4 + u) * GP + co * 8]) = z;
   }
 }
 
 template <int MODE>
 __device__ __forceinline__ void gemm_store(bf16* As, bf16* Bs, const Stage& sg, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + 256 * i;
-    *reinterpret_cast<bf16x8*>(&As[(v >> 3) * GP + (v & 7) * 8]) = sg.a[i];
-  }
-  if constexpr (MODE == kOut) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + 256 * i;
-      *reinterpret_cast<bf16x8*>(&Bs[(v >> 3) * GP + (v & 7) * 8]) = sg.b[i];
-    }
-  } else {
-    // GN(x) = a x + s in fp32, rounded once to bf16; b[e] = token e's 8 channels
-    bf16x8 b[4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float a = sg.cf[j >> 1][(j & 1) * 2], sh = sg.cf[j >> 1][(j & 1) * 2 + 1];
-      const u32x2 v = sg.xr[j];
-      const float xv[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
-                           __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e][j] = static_cast<bf16>(fmaf(a, xv[e], sh));
-    }
-    const int tq = qkv_tq(tid), co = qkv_co(tid);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<bf16x8*>(&Bs[(tq * 4 + e) * GP + co * 8]) = b[e];
-  }
+  for (int u = 0; u < 4; ++u) store_part<MODE>(As, Bs, sg, tid, u);
 }
 
+// Sub-step s (16 channels) of one k-step: 2 x 2 MFMAs on fragments read from LDS.
 template <bool TR>
-__device__ __forceinline__ void gemm_compute(f32x16 (&acc)[2][2], const bf16* As, const bf16* Bs,
-                                             int wm, int wn, int half, int col) {
+__device__ __forceinline__ void compute_sub(f32x16 (&acc)[2][2], const bf16* As, const bf16* Bs,
+                                            int wm, int wn, int half, int col, int s) {
+  const int kofs = s * 16 + half * 8;
+  bf16x8 fa[2], fb[2];
 #pragma unroll
-  for (int s = 0; s < GK / 16; ++s) {
-    const int kofs = s * 16 + half * 8;
-    bf16x8 fa[2], fb[2];
+  for (int i = 0; i < 2; ++i)
+    fa[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + col) * GP + kofs]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      fa[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + col) * GP + kofs]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + col) * GP + kofs]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
-                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// acc[i][j]: channel block i x token block j of the wave's quadrant.
-// TR = false: rows are channels; TR = true: rows are tokens.
-// The loads of k-step s+1 are issued right after the barrier of step s and
-// land in LDS (normalised, for Q/K/V) after step s's MFMAs.
-template <int MODE, bool TR>
-__device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], const ProjParams& pp, bf16* lds,
-                                          int m0, int n0, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int half = lane >> 5, col = lane & 31;
+  for (int j = 0; j < 2; ++j)
+    fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + col) * GP + kofs]);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  LoadCtx lc;
-  gemm_setup<MODE>(lc, pp, m0, n0, tid);
-  const int nk = pp.C / GK;  // >= 1
-  constexpr int BUF = (GM + GN) * GP;
-  Stage sg;
-  gemm_load<MODE>(sg, lc, 0);
-  gemm_store<MODE>(lds, lds + GM * GP, sg, tid);
-  for (int ks = 0; ks < nk; ++ks) {
-    __syncthreads();  // buffer ks&1 is complete; buffer (ks+1)&1 is no longer read
-    if (ks + 1 < nk) gemm_load<MODE>(sg, lc, (ks + 1) * GK);
-    const bf16* As = lds + (ks & 1) * BUF;
-    gemm_compute<TR>(acc, As, As + GM * GP, wm, wn, half, col);
-    if (ks + 1 < nk) {
-      bf16* Ad = lds + ((ks + 1) & 1) * BUF;
-      gemm_store<MODE>(Ad, Ad + GM * GP, sg, tid);
-    }
-  }
+      acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// Epilogue: each wave stages its 64 x 64 quadrant in its own LDS region in
-// the destination's layout (bias added; Q scaled), then stores it with
-// coalesced vectors.
+// Epilogue geometry: each wave stages its 64 x 64 quadrant in its own LDS
+// region in the destination's layout (bias added; Q scaled), then stores it
+// with coalesced vectors.
 //  * Q / K: E[token][channel] bf16; a lane stores 16-byte runs of 8 channels
 //    of one token, 8 lanes covering one token's 64 channels.
 //  * V: E[channel][token] bf16; a lane owns one run of 4 tokens and stores it
@@ -473,62 +438,187 @@ __device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], const ProjParams&
 // Staging pitches (elements): 144-byte bf16 rows and 272-byte fp32 rows keep
 // the 8- and 16-byte staging writes of 16 lanes on distinct banks.
 constexpr int EPB = 72, EPF = 68;
+static_assert(2 * 64 * EPF * 4 <= (GM + GN) * GP * 2, "two fp32 staging regions fit one buffer");
 
 struct EpiCtx {
-  int mw, nw;            // first row / token of the wave's quadrant
+  int mw, nw;            // first row / token of the wave's quadrant (wave-uniform)
   int lane, half, col;
 };
 
+// What the epilogue reads from global memory, fetched before the last k-steps'
+// MFMAs so that its latency is hidden behind them rather than paid once per
+// store: the bias values of the lane's channels and, for the output
+// projection, the residual x of the lane's 16 store runs.
+struct EpiPre {
+  bf16x4 qk_bias[2][4];  // Q / K: channels i*32 + 8g + 4*half + 0..3
+  float col_bias[2];     // V / output: channel i*32 + col
+  u32x2 res[16];         // output: x at the 16 runs epi_store writes
+};
+
+// The bias of the wave's rows (NULL: no bias), selected with a uniform branch
+// so the pointer comes from the kernel arguments, not from a dynamic index.
+__device__ __forceinline__ const bf16* row_bias(const ProjParams& pp, int which) {
+  return static_cast<const bf16*>(which == 0 ? pp.bias[0] : which == 1 ? pp.bias[1] : pp.bias[2]);
+}
+
+// Residual run u of a lane (output projection): channel row ec.mw + 4u + (lane >> 4)
+// of sample b, tokens t .. t+3 of this lane's run; byte offsets into x.
+__device__ __forceinline__ bool res_run(const ProjParams& pp, const EpiCtx& ec, int& b, int& t) {
+  const int nn = ec.nw + 4 * (ec.lane & 15);
+  if (nn >= pp.NT) return false;  // NT % 4 == 0: a run is all in or all out
+  b = int(unsigned(nn) / unsigned(pp.T));
+  t = nn - b * pp.T;
+  return true;
+}
+
 template <int MODE, bool TR>
-__device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const ProjParams& pp,
-                                          bf16* lds, int wave, const EpiCtx& ec) {
+__device__ __forceinline__ void epi_prefetch(EpiPre& ep, const ProjParams& pp, const EpiCtx& ec) {
+  const int C = pp.C;
+  if (ec.mw >= pp.M) return;  // the upper half of a 64-row last tile stores nothing
+  if constexpr (MODE == kOut) {
+    const bf16* bp = row_bias(pp, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ep.col_bias[i] = bp ? static_cast<float>(bp[ec.mw + i * 32 + ec.col]) : 0.f;
+    int b = 0, t = 0;
+    const bool ok = res_run(pp, ec, b, t);
+    // out-of-range runs read offset 0x80000000, past the resource: zeros
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(pp.x, unsigned(pp.NT) * unsigned(C) * 2u);
+    const unsigned v0 = ok ? ((unsigned(b) * unsigned(C) + unsigned(ec.mw + (ec.lane >> 4))) *
+                                  unsigned(pp.T) + unsigned(t)) * 2u
+                           : 0x80000000u;
+    const unsigned row4 = unsigned(pp.T) * 8u;  // four channel rows
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      ep.res[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, int(v0), int(u * row4), 0));
+  } else if constexpr (TR) {  // V
+    const bf16* bp = row_bias(pp, 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ep.col_bias[i] = bp ? static_cast<float>(bp[ec.mw - 2 * C + i * 32 + ec.col]) : 0.f;
+  } else {  // Q or K
+    const int which = ec.mw / C;
+    const bf16* bp = row_bias(pp, which);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        ep.qk_bias[i][g] = bp ? *reinterpret_cast<const bf16x4*>(bp + (ec.mw - which * C) + i * 32 +
+                                                                 8 * g + 4 * ec.half)
+                              : bf16x4{};
+  }
+}
+
+// acc[i][j]: channel block i x token block j of the wave's quadrant.
+// TR = false: rows are channels; TR = true: rows are tokens.
+// Two LDS buffers (distinct arrays, so the compiler may interleave their
+// accesses) and two register stages.  Step s: after the barrier the loads of
+// step s+2 go out into one register stage; step s+1, loaded during step s-1,
+// is written (for Q/K/V normalised) from the other into the buffer step s-1
+// read, while the MFMAs of step s read the other buffer.  The epilogue's own
+// loads go out before the last two steps.
+template <int MODE, bool TR>
+__device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], EpiPre& ep, const ProjParams& pp,
+                                          bf16* lds0, bf16* lds1, int m0, int n0, int tid,
+                                          int wave, const EpiCtx& ec) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = ec.half, col = ec.col;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  LoadCtx lc;
+  gemm_setup<MODE>(lc, pp, m0, n0, tid);
+  const int nk = pp.C / GK;  // >= 1
+  Stage s0, s1;
+  gemm_load<MODE>(s0, lc, 0);
+  gemm_store<MODE>(lds0, lds0 + GM * GP, s0, tid);
+  if (nk > 1) gemm_load<MODE>(s1, lc, GK);
+  // rd: step ks's buffer; wr: the other one, which receives step ks+1 from
+  // `nxt` (when `more`); `fre` receives the loads of step ks+2 (when `load`).
+  auto step = [&](int ks, const bf16* rd, bf16* wr, const Stage& nxt, Stage& fre, bool more,
+                  bool load) {
+    __syncthreads();  // rd is complete; wr is no longer read
+    if (load) gemm_load<MODE>(fre, lc, (ks + 2) * GK);
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top of the step
+    // sub-step u's MFMAs, then part u of the next stage, so that the in-order
+    // issue of a wave puts the normalisation between its own MFMAs
+#pragma unroll
+    for (int u = 0; u < GK / 16; ++u) {
+      compute_sub<TR>(acc, rd, rd + GM * GP, wm, wn, half, col, u);
+      if (more) store_part<MODE>(wr, wr + GM * GP, nxt, tid, u);
+    }
+  };
+  // Which register stage and buffer a step uses is fixed at compile time in
+  // each branch (chosen at run time, both stages would stay live in the tail).
+  const int body = nk > 2 ? nk - 2 : 0;  // steps that still load
+  if (nk == 1) {
+    epi_prefetch<MODE, TR>(ep, pp, ec);
+    step(0, lds0, lds1, s1, s0, false, false);
+  } else if (body & 1) {
+    step(0, lds0, lds1, s1, s0, true, true);
+    for (int ks = 1; ks < body; ks += 2) {
+      step(ks, lds1, lds0, s0, s1, true, true);
+      step(ks + 1, lds0, lds1, s1, s0, true, true);
+    }
+    epi_prefetch<MODE, TR>(ep, pp, ec);
+    step(body, lds1, lds0, s0, s1, true, false);
+    step(body + 1, lds0, lds1, s1, s0, false, false);
+  } else {
+    for (int ks = 0; ks < body; ks += 2) {
+      step(ks, lds0, lds1, s1, s0, true, true);
+      step(ks + 1, lds1, lds0, s0, s1, true, true);
+    }
+    epi_prefetch<MODE, TR>(ep, pp, ec);
+    step(body, lds0, lds1, s1, s0, true, false);
+    step(body + 1, lds1, lds0, s0, s1, false, false);
+  }
+}
+
+template <int MODE, bool TR>
+__device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const EpiPre& ep,
+                                          const ProjParams& pp, bf16* stg, const EpiCtx& ec) {
   const int C = pp.C, half = ec.half, col = ec.col;
   if constexpr (MODE == kOut) {
-    float* E = reinterpret_cast<float*>(lds) + wave * 64 * EPF;
+    float* E = reinterpret_cast<float*>(stg);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int cl = i * 32 + col;
-      const bf16* bp = static_cast<const bf16*>(pp.bias[0]);  // NULL: no bias
-      const float bias = bp ? static_cast<float>(bp[ec.mw + cl]) : 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + bias;
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + ep.col_bias[i];
           *reinterpret_cast<f32x4*>(&E[cl * EPF + j * 32 + 8 * g + 4 * half]) = v;
         }
     }
   } else if constexpr (TR) {  // V
-    bf16* E = lds + wave * 64 * EPB;
-    const bf16* bias = static_cast<const bf16*>(pp.bias[2]);  // NULL: no bias
+    bf16* E = stg;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int cl = i * 32 + col;
-      const float bv = bias ? static_cast<float>(bias[ec.mw - 2 * C + cl]) : 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           bf16x4 pk;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(acc[i][j][4 * g + e] + bv);
+          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(acc[i][j][4 * g + e] + ep.col_bias[i]);
           *reinterpret_cast<bf16x4*>(&E[cl * EPB + j * 32 + 8 * g + 4 * half]) = pk;
         }
     }
   } else {  // Q or K
-    bf16* E = lds + wave * 64 * EPB;
-    const int which = ec.mw / C;
-    const float sc = which == 0 ? pp.q_scale : 1.f;
-    const bf16* bias = static_cast<const bf16*>(pp.bias[which]);  // NULL: no bias
+    bf16* E = stg;
+    const float sc = ec.mw < C ? pp.q_scale : 1.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int cl = i * 32 + 8 * g + 4 * half;
-        const bf16x4 bv = bias ? *reinterpret_cast<const bf16x4*>(bias + (ec.mw - which * C) + cl)
-                               : bf16x4{};
+        const bf16x4 bv = ep.qk_bias[i][g];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           bf16x4 pk;
@@ -542,32 +632,31 @@ __device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const ProjP
 }
 
 template <int MODE, bool TR>
-__device__ __forceinline__ void epi_store(const ProjParams& pp, const bf16* lds, int wave,
+__device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp, const bf16* stg,
                                           const EpiCtx& ec) {
   const int C = pp.C, T = pp.T, lane = ec.lane;
   if constexpr (MODE == kOut || TR) {
     const int tq = lane & 15;  // this lane's run of 4 tokens
-    const int nn = ec.nw + 4 * tq;
-    if (nn >= pp.NT) return;   // NT % 4 == 0: a run is all in or all out
-    const int b = int(unsigned(nn) / unsigned(T));
-    const int t = nn - b * T;
+    int b = 0, t = 0;
+    if (!res_run(pp, ec, b, t)) return;
     if constexpr (MODE == kOut) {
-      const float* E = reinterpret_cast<const float*>(lds) + wave * 64 * EPF;
-      const bf16* x = static_cast<const bf16*>(pp.x);
+      const float* E = reinterpret_cast<const float*>(stg);
       bf16* out = static_cast<bf16*>(pp.out);
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int cl = 4 * u + (lane >> 4);
         const int64_t idx = (int64_t(b) * C + ec.mw + cl) * T + t;
-        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(x + idx);
+        const u32x2 xr = ep.res[u];
+        const float xv[4] = {__uint_as_float(xr[0] << 16), __uint_as_float(xr[0] & 0xffff0000u),
+                             __uint_as_float(xr[1] << 16), __uint_as_float(xr[1] & 0xffff0000u)};
         const f32x4 y = *reinterpret_cast<const f32x4*>(&E[cl * EPF + 4 * tq]);
         bf16x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(static_cast<float>(xv[e]) + y[e]);
+        for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(xv[e] + y[e]);
         *reinterpret_cast<bf16x4*>(out + idx) = pk;
       }
     } else {
-      const bf16* E = lds + wave * 64 * EPB;
+      const bf16* E = stg;
       bf16* vt = static_cast<bf16*>(pp.vt);
       const int slot = vt_slot(t);  // aligned runs of 4 tokens keep their order
       const int cw = ec.mw - 2 * C;
@@ -581,7 +670,7 @@ __device__ __forceinline__ void epi_store(const ProjParams& pp, const bf16* lds,
       }
     }
   } else {
-    const bf16* E = lds + wave * 64 * EPB;
+    const bf16* E = stg;
     const int which = ec.mw / C;
     bf16* dst = static_cast<bf16*>(which == 0 ? pp.q : pp.k);
     const int q8 = lane & 7;  // this lane's 8-channel run
@@ -607,9 +696,11 @@ __device__ __forceinline__ void epi_store(const ProjParams& pp, const bf16* lds,
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(ProjParams pp, int mtiles) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (GM + GN) * GP];
+  __shared__ __attribute__((aligned(16))) bf16 lds0[(GM + GN) * GP];
+  __shared__ __attribute__((aligned(16))) bf16 lds1[(GM + GN) * GP];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lid = xcd_remap_gemm(int(blockIdx.x), int(gridDim.x));
   const int m0 = (lid % mtiles) * GM;
   const int n0 = (lid / mtiles) * GN;
@@ -623,18 +714,34 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(ProjParams pp, int mt
   const bool tr = MODE == kOut || ec.mw >= 2 * pp.C;
   const bool valid = ec.mw < pp.M;  // false for the upper half of a 64-row last tile
   f32x16 acc[2][2];
+  EpiPre ep;
+  // the wave's staging region: two per buffer (two fp32 regions fit one buffer)
+  bf16* stg = (wave < 2 ? lds0 : lds1) + (wave & 1) * 64 * EPF * 2;
+  // The epilogue works on copies that the compiler cannot see through, so that
+  // its index arithmetic (divisions by T and d, lane offsets) is not hoisted
+  // above the main loop, where it would hold registers the loop needs.
+  auto epilogue_inputs = [&](ProjParams& pe, EpiCtx& ee) {
+    pe = pp;
+    ee = ec;
+    asm volatile("" : "+s"(pe.T), "+s"(pe.d), "+s"(pe.n), "+s"(pe.Tp));
+    asm volatile("" : "+v"(ee.lane), "+v"(ee.half), "+v"(ee.col));
+  };
+  ProjParams pe;
+  EpiCtx ee;
   if (tr) {
-    gemm_main<MODE, true>(acc, pp, lds, m0, n0, tid);
+    gemm_main<MODE, true>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
+    epilogue_inputs(pe, ee);
     __syncthreads();  // every wave is done reading the operand tiles
-    if (valid) epi_stage<MODE, true>(acc, pp, lds, wave, ec);
+    if (valid) epi_stage<MODE, true>(acc, ep, pe, stg, ee);
     __syncthreads();
-    if (valid) epi_store<MODE, true>(pp, lds, wave, ec);
+    if (valid) epi_store<MODE, true>(ep, pe, stg, ee);
   } else {
-    gemm_main<MODE, false>(acc, pp, lds, m0, n0, tid);
+    gemm_main<MODE, false>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
+    epilogue_inputs(pe, ee);
     __syncthreads();
-    if (valid) epi_stage<MODE, false>(acc, pp, lds, wave, ec);
+    if (valid) epi_stage<MODE, false>(acc, ep, pe, stg, ee);
     __syncthreads();
-    if (valid) epi_store<MODE, false>(pp, lds, wave, ec);
+    if (valid) epi_store<MODE, false>(ep, pe, stg, ee);
   }
 }
 
