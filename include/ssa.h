@@ -39,7 +39,9 @@
  * - B == 0, H == 0 or W == 0 is an empty input: SSA_OK, nothing launched, and
  *   the data pointers may be NULL.
  * - Supported: fp32 with 1 <= d <= 128; bf16 (fp32 accumulation) with
- *   d in {32, 64, 96, 128}.  Other head sizes return SSA_E_UNSUPPORTED.
+ *   d in {32, 64, 96, 128}.  Other head sizes return SSA_E_UNSUPPORTED, and
+ *   so does a call with 3*B*H*W*C >= 2^31 (the Q|K|V projection's output
+ *   must stay below 2^31 elements; every tensor then fits 32-bit offsets).
  *
  * Workspace (bytes from ssa_workspace_size; regions from
  * ssa_get_workspace_layout, each 256-byte aligned):

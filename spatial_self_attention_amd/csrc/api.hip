@@ -256,7 +256,7 @@ const char* ssa_status_string(int status) {
     case SSA_E_DTYPE: return "unknown dtype";
     case SSA_E_UNSUPPORTED:
       return "unsupported size: head size must be 1..128 (fp32) or 32/64/96/128 (bf16), even "
-             "with rotary embeddings, and each tensor below 2^31 elements";
+             "with rotary embeddings, and 3*B*H*W*C below 2^31";
     case SSA_E_WORKSPACE: return "workspace smaller than ssa_workspace_size()";
     case SSA_E_ALIAS: return "out or workspace overlaps another buffer";
     case SSA_E_ALIGN: return "a pointer is not 16-byte aligned";

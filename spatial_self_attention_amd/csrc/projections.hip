@@ -326,34 +326,36 @@ __device__ __forceinline__ int qkv_co(int tid) { return ((tid >> 2) & 3) | ((tid
 template <int MODE>
 __device__ __forceinline__ void gemm_setup(LoadCtx& lc, const ProjParams& pp, int m0, int n0,
                                            int tid) {
-  const int C = pp.C;
-  const uint32_t wbytes = uint32_t(C) * uint32_t(C) * 2u;
+  // Byte offsets are formed in 32-bit unsigned arithmetic: a tensor holds at
+  // most 2^31 - 1 elements, so a bf16 offset stays below 2^32 but may pass 2^31.
+  const unsigned C = unsigned(pp.C);
+  const uint32_t wbytes = C * C * 2u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rb = m0 + 32 * i < pp.M ? m0 + 32 * i : 0;
-    const int which = MODE == kQkv ? rb / C : 0;
+    const int which = MODE == kQkv ? rb / int(C) : 0;
     lc.ra[i] = make_rsrc(pp.w[which], wbytes);
-    lc.sa[i] = (rb - which * C) * C * 2;
+    lc.sa[i] = int((unsigned(rb) - unsigned(which) * C) * C * 2u);
   }
-  lc.va = ((tid >> 3) * C + (tid & 7) * 8) * 2;
+  lc.va = int((unsigned(tid >> 3) * C + unsigned(tid & 7) * 8u) * 2u);
   if constexpr (MODE == kOut) {
-    lc.rb = make_rsrc(pp.o, uint32_t(pp.NT) * uint32_t(C) * 2u);
+    lc.rb = make_rsrc(pp.o, uint32_t(pp.NT) * C * 2u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int nn = min(n0 + (tid >> 3) + 32 * i, pp.NT - 1);
-      lc.vb[i] = (nn * C + (tid & 7) * 8) * 2;
+      const int nn = min(n0 + (tid >> 3) + 32 * i, int(pp.NT) - 1);
+      lc.vb[i] = int((unsigned(nn) * C + unsigned(tid & 7) * 8u) * 2u);
     }
   } else {
-    const int T = pp.T;
+    const unsigned T = unsigned(pp.T);
     const int tq = qkv_tq(tid), co = qkv_co(tid);
-    const int nn = min(n0 + tq * 4, pp.NT - 4);
-    const int b = int(unsigned(nn) / unsigned(T));
-    const int t = nn - b * T;
-    lc.rb = make_rsrc(pp.x, uint32_t(pp.NT) * uint32_t(C) * 2u);
-    lc.rc = make_rsrc(pp.coef, uint32_t(pp.NT / T) * uint32_t(C) * 8u);
-    lc.vx = ((b * C + co * 8) * T + t) * 2;
-    lc.vc = (b * C + co * 8) * 8;
-    lc.xrow = T * 2;
+    const int nn = min(n0 + tq * 4, int(pp.NT) - 4);
+    const unsigned b = unsigned(nn) / T;
+    const unsigned t = unsigned(nn) - b * T;
+    lc.rb = make_rsrc(pp.x, uint32_t(pp.NT) * C * 2u);
+    lc.rc = make_rsrc(pp.coef, uint32_t(pp.NT / pp.T) * C * 8u);
+    lc.vx = int(((b * C + unsigned(co) * 8u) * T + t) * 2u);
+    lc.vc = int((b * C + unsigned(co) * 8u) * 8u);
+    lc.xrow = int(T * 2u);
   }
 }
 
@@ -372,7 +374,7 @@ __device__ __forceinline__ void gemm_load(Stage& sg, const LoadCtx& lc, int k0) 
     // per-thread offset serves all eight loads
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      sg.xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(lc.rb, lc.vx, (k0 + j) * lc.xrow, 0));
+      sg.xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(lc.rb, lc.vx, int(unsigned(k0 + j) * unsigned(lc.xrow)), 0));
   }
 }
 

@@ -131,6 +131,12 @@ OK_SHAPE = (2, 64, 4, 4, 8, 2, ssa.SSA_BF16)
     ("fp32 d = 256", dict(shape=(2, 256, 4, 4, 8, 1, ssa.SSA_F32)), "SSA_E_UNSUPPORTED"),
     ("too many elements", dict(shape=(1 << 20, 512, 64, 64, 32, 4, ssa.SSA_BF16)),
      "SSA_E_UNSUPPORTED"),
+    # the size limit is exact: 3*B*T*C = 2,147,352,576 passes (and stops at the
+    # workspace check: nothing launches), one more sample does not
+    ("largest accepted size", dict(shape=(5461, 512, 16, 16, 32, 8, ssa.SSA_BF16), ws_bytes=1024),
+     "SSA_E_WORKSPACE"),
+    ("one sample past the size limit", dict(shape=(5462, 512, 16, 16, 32, 8, ssa.SSA_BF16)),
+     "SSA_E_UNSUPPORTED"),
     ("null x", dict(shape=OK_SHAPE, ptr={"x": 0}), "SSA_E_NULL"),
     ("null out", dict(shape=OK_SHAPE, ptr={"out": 0}), "SSA_E_NULL"),
     # biases are nullable: a NULL bias passes the pointer checks and the call

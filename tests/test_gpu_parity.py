@@ -204,6 +204,44 @@ def test_full_size_sampled(idx, stress):
     assert worst <= TOL[wl.dtype]
 
 
+def test_largest_accepted_call():
+    """The largest size the library accepts, 3*B*T*C just below 2^31: x, out
+    and each of Q, K, V^T, O hold 7.2e8 bf16 elements (1.43e9 bytes, the
+    kernels' largest 32-bit offsets).  x ~ N(0, 1) is drawn on the GPU (a
+    seeded torch generator); the block is checked against the oracle on
+    sampled pixels of the first, a middle and the last sample, each sample's
+    slice upcast on its own."""
+    wl = Workload("largest call", "bf16", 5461, 512, 16, 16, 32, 8)
+    n_el = wl.B * wl.C * wl.T
+    assert 3 * n_el < 2 ** 31 - 1 < 3 * (n_el + wl.C * wl.T)
+    gen = torch.Generator(device=DEV).manual_seed(2024)
+    xg = torch.empty((wl.B, wl.C, wl.H, wl.W), dtype=torch.bfloat16, device=DEV)
+    for b0 in range(0, wl.B, 1024):  # fp32 draws in slices: bounded temporaries
+        b1 = min(b0 + 1024, wl.B)
+        xg[b0:b1] = torch.randn((b1 - b0, wl.C, wl.H, wl.W), generator=gen, device=DEV)
+    _, p = draw(wl.replace(B=1), 77)
+    pg = {k: v.to(DEV) for k, v in p.items()}
+    out = torch.empty_like(xg)
+    ws = ssa.workspace_for(xg, wl.num_groups, wl.num_heads)
+    print(f"[gpu] {wl.name}: B={wl.B} C={wl.C} T={wl.T} n={wl.num_heads}, "
+          f"{2 * n_el / 2 ** 30:.2f} GiB per tensor", flush=True)
+    ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws)
+    torch.cuda.synchronize()
+    _, p64 = to_f64(xg[:1].cpu(), p)
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for b in (0, wl.B // 2, wl.B - 1):
+        x64 = xg[b:b + 1].double().cpu().numpy()
+        rows = np.unique(np.concatenate([[0, wl.T - 1], rng.integers(0, wl.T, 6)]))
+        want = ORA.forward_pixels(x64, p64, wl.num_groups, wl.num_heads, 0, rows)
+        got = out[b].double().cpu().numpy().reshape(wl.C, wl.T)[:, rows]
+        assert np.isfinite(got).all()
+        e = float(np.max(np.abs(got - want))) / float(np.max(np.abs(want)))
+        worst = max(worst, e)
+    print(f"  sampled err {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # Behaviour
 # ---------------------------------------------------------------------------
