@@ -408,24 +408,31 @@ __device__ __forceinline__ void gemm_store(bf16* As, bf16* Bs, const Stage& sg, 
   for (int u = 0; u < 4; ++u) store_part<MODE>(As, Bs, sg, tid, u);
 }
 
-// Sub-step s (16 channels) of one k-step: 2 x 2 MFMAs on fragments read from LDS.
-template <bool TR>
-__device__ __forceinline__ void compute_sub(f32x16 (&acc)[2][2], const bf16* As, const bf16* Bs,
-                                            int wm, int wn, int half, int col, int s) {
+// Operand fragments of sub-step s (16 channels) of one k-step, read from LDS.
+struct Frags {
+  bf16x8 a[2], b[2];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const bf16* As, const bf16* Bs, int wm,
+                                           int wn, int half, int col, int s) {
   const int kofs = s * 16 + half * 8;
-  bf16x8 fa[2], fb[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    fa[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + col) * GP + kofs]);
+    f.a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + col) * GP + kofs]);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + col) * GP + kofs]);
+    f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + col) * GP + kofs]);
+}
+
+// The 2 x 2 MFMAs of one sub-step.
+template <bool TR>
+__device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const Frags& f) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
-                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // Epilogue geometry: each wave stages its 64 x 64 quadrant in its own LDS
@@ -545,10 +552,21 @@ __device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], EpiPre& ep, const
     if (load) gemm_load<MODE>(fre, lc, (ks + 2) * GK);
     __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top of the step
     // sub-step u's MFMAs, then part u of the next stage, so that the in-order
-    // issue of a wave puts the normalisation between its own MFMAs
+    // issue of a wave puts the normalisation between its own MFMAs.  The
+    // output projection (fewer work-groups per CU to hide LDS latency, and
+    // registers to spare) reads the fragments of sub-step u+1 before sub-step
+    // u's MFMAs.
+    constexpr bool kAhead = MODE == kOut;
+    Frags f[2];
+    if (kAhead) read_frags(f[0], rd, rd + GM * GP, wm, wn, half, col, 0);
 #pragma unroll
     for (int u = 0; u < GK / 16; ++u) {
-      compute_sub<TR>(acc, rd, rd + GM * GP, wm, wn, half, col, u);
+      if (kAhead) {
+        if (u + 1 < GK / 16) read_frags(f[(u + 1) & 1], rd, rd + GM * GP, wm, wn, half, col, u + 1);
+      } else {
+        read_frags(f[u & 1], rd, rd + GM * GP, wm, wn, half, col, u);
+      }
+      mfma_sub<TR>(acc, f[u & 1]);
       if (more) store_part<MODE>(wr, wr + GM * GP, nxt, tid, u);
     }
   };
