@@ -437,25 +437,42 @@ __device__ __forceinline__ void init_state(AttnState<D, QB>& st, const bf16* Q, 
 }
 
 // O = O^T accumulators / l, token-major (B, T, C) with heads concatenated.
+// A lane holds runs of 4 dims of one query, so the wave first stages its
+// 32*QB queries x D in LDS (rows of D + 8 bf16, its own region `stg`), then
+// stores 16 bytes per lane with each query's D dims contiguous: whole rows of
+// the output instead of 8-byte pieces of 32 rows per instruction.
 template <int D, int QB>
 __device__ __forceinline__ void write_o(const AttnState<D, QB>& st, const AttnParams& ap, int b,
-                                        int head, int qbase, int half, int col) {
+                                        int head, int qbase, int half, int col, int lane,
+                                        bf16* stg) {
+  constexpr int EP = D + 8;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qbase + qb * 32 + col;
     const float inv = 1.0f / halves_sum(st.l[qb]);
-    if (qi < ap.T) {
-      bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * ap.T + qi) * ap.C + head * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 pk;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 pk;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(st.o[qb][db][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(O + db * 32 + 8 * g + 4 * half) = pk;
-        }
-    }
+        for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(st.o[qb][db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(&stg[(qb * 32 + col) * EP + db * 32 + 8 * g + 4 * half]) = pk;
+      }
+  }
+  // the wave reads what its own lanes wrote: LDS operations of one wave stay in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int CPR = D / 8;  // 16-byte chunks per query row
+  bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * ap.T) * ap.C + head * D;
+#pragma unroll
+  for (int i = 0; i < QB * D / 16; ++i) {
+    const int c = lane + 64 * i;
+    const int q = c / CPR, dc = c % CPR;
+    const int qi = qbase + q;
+    if (qi < ap.T)
+      *reinterpret_cast<bf16x8*>(O + int64_t(qi) * ap.C + dc * 8) =
+          *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]);
   }
 }
 
@@ -528,7 +545,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL ? 2 : attn_min_blocks<D>())
                                       nfull == 0, rp);
   }
 
-  write_o<D, QB>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col);
+  __syncthreads();  // every wave is done with the key tiles: LDS becomes staging
+  static_assert(NW * 32 * QB * (D + 8) <= 2 * TL::BUF, "output staging fits the tile buffers");
+  write_o<D, QB>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col, lane,
+                 lds + wave * 32 * QB * (D + 8));
 }
 
 // ---------------------------------------------------------------------------
