@@ -1,6 +1,7 @@
 """Throughput of the spatial self-attention block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I] [--no-cpu]
+                    [--options relpos,qknorm,rope]
 
 A step is one ssa_forward over one batch of the selected workload (GroupNorm
 statistics, QKV projection, flash attention, output projection + residual),
@@ -16,6 +17,12 @@ Also reported:
   HBM bandwidth), with HBM traffic from the stored rocprofv3 counter summary
   when it was taken on the current kernel sources;
 * the fp64 CPU oracle's rate on a bounded sample of the same workload.
+
+With --options the step is ssa_forward_ex with the listed optional steps
+(2-D relative-position logit bias, per-head query/key normalisation, rotary
+embeddings; tensors drawn as in the tests); only the whole step is timed
+(the per-stage entry point runs the plain block), so the per-kernel breakdown,
+the roofline object and the CPU baseline are null.
 """
 from __future__ import annotations
 
@@ -114,6 +121,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--options", default="",
+                    help="comma list of optional steps to switch on: relpos, qknorm, rope")
     ap.add_argument("--graph", action="store_true",
                     help="time K steps replayed from one HIP graph instead of eager launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -137,7 +146,7 @@ def main():
     import torch
 
     import spatial_self_attention_amd as ssa
-    from spatial_self_attention_amd.inputs import WORKLOADS, default_seed, draw
+    from spatial_self_attention_amd.inputs import WORKLOADS, default_seed, draw, draw_options
 
     wl = WORKLOADS[args.config]
     seed = default_seed(args.config)
@@ -148,9 +157,20 @@ def main():
     out = torch.empty_like(xg)
     ws = ssa.workspace_for(xg, wl.num_groups, wl.num_heads)
     stream = torch.cuda.current_stream(dev)
+    names = [o for o in args.options.split(",") if o]
+    unknown = set(names) - {"relpos", "qknorm", "rope"}
+    if unknown:
+        ap.error(f"unknown options {sorted(unknown)}")
+    opts = None
+    if names:
+        od = draw_options(wl, seed, rel_pos="relpos" in names, qk_norm="qknorm" in names,
+                          rope="rope" in names)
+        odg = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in od.items()}
+        opts = ssa.make_options(xg, wl.num_heads, odg["rel_pos_table"], odg["q_norm_gamma"],
+                                odg["k_norm_gamma"], odg["rope"])
 
     def step():  # on torch's current stream (the capture stream inside a graph)
-        ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws)
+        ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws, options=opts)
 
     for _ in range(args.warmup):
         step()
@@ -180,6 +200,19 @@ def main():
     elapsed = max(wall, gpu_s)
     ms_per_step = elapsed / args.steps * 1e3
     tflops = wl.flops() * args.steps / elapsed / 1e12
+
+    if opts is not None:
+        print(json.dumps({
+            "metric": "block TFLOP/s", "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+            "data": "synthetic (seeded, workload distributions)",
+            "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
+                       "num_groups": wl.num_groups, "num_heads": wl.num_heads, "d": wl.d,
+                       "launch": "graph" if args.graph else "eager", "options": names},
+            "kernels": None, "roofline": None, "cpu_baseline": None,
+            "source_digest": source_digest()}), flush=True)
+        return
 
     # ---- per-kernel durations: each stage replayed back-to-back from a graph ----
     reps = max(20, min(args.steps, 200))

@@ -258,30 +258,66 @@ __device__ __forceinline__ float probs(bf16x8 (&pb)[2], const f32x16& s, float d
 // after the P V products already issued for earlier sub-blocks.
 // Relative-position bias of one wave's queries (HNDL attention operator,
 // "Relative position bias"): column `head` of the table (stride n), and the
-// grid row / column of each of the wave's query blocks' lane query.
+// grid row / column of each of the wave's query blocks' lane query.  REL = 1
+// gathers every entry from the table in global memory; REL = 2 reads it from
+// `slice`, the part of the head's column the current key tile needs (table
+// rows lo .., staged in LDS with the tile).
 template <int QB>
 struct RelPos {
   const bf16* tab;   // table + head
   int H, W, n;
   int qr[QB], qc[QB];
+  const bf16* slice;  // REL = 2: LDS copy of table rows lo .. of this head
+  int lo;
+  int qrow[QB];       // REL = 2: (row(q) + H - 1)(2W - 1) + col(q) + W - 1 - lo
 };
+
+// Entries of the table slice one work-group stages per key tile (REL = 2).
+constexpr int kRelSlice = 1024;
+
+// Table rows (first, count) that queries q0..q1 meet against keys k0..k1.
+// A row is (dr + H - 1)(2W - 1) + (dc + W - 1) with dr = row(q) - row(k) and
+// dc = col(q) - col(k), 0 <= dc + W - 1 < 2W - 1: the rows are ordered by
+// (dr, dc), so the extreme (dr, dc) pairs bound them.
+__device__ __forceinline__ void rel_rows(int q0, int q1, int k0, int k1, int H, int W, int& lo,
+                                         int& len) {
+  const int qr0 = q0 / W, qr1 = q1 / W, kr0 = k0 / W, kr1 = k1 / W;
+  const int qc0 = qr0 == qr1 ? q0 - qr0 * W : 0, qc1 = qr0 == qr1 ? q1 - qr0 * W : W - 1;
+  const int kc0 = kr0 == kr1 ? k0 - kr0 * W : 0, kc1 = kr0 == kr1 ? k1 - kr0 * W : W - 1;
+  lo = (qr0 - kr1 + H - 1) * (2 * W - 1) + (qc0 - kc1 + W - 1);
+  len = (qr1 - kr0 + H - 1) * (2 * W - 1) + (qc1 - kc0 + W - 1) - lo + 1;
+}
 
 // Adds log2(e) * table[(row(q)-row(k)+H-1)(2W-1) + col(q)-col(k)+W-1, head]
 // to the scores of one 32-key sub-block (keys >= T are left alone: masked).
-template <int QB>
+template <int QB, int REL>
 __device__ __forceinline__ void add_rel(f32x16 (&s)[QB], const RelPos<QB>& rp, int kfirst, int T,
                                         int half) {
 #pragma unroll
   for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
     const int k0 = kfirst + 8 * run + 4 * half;
     int kr = k0 / rp.W, kc = k0 - kr * rp.W;
+    if (REL == 2 && kc + 3 < rp.W && k0 + 3 < T) {
+      // four keys in one grid row: their table rows are consecutive (row(q) -
+      // row(k) fixed, col(k) + e), i.e. four adjacent slice entries, read
+      // backwards from one address
+      const int kterm = kr * (2 * rp.W - 1) + kc;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bf16* p = rp.slice + (rp.qrow[qb] - kterm - 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[qb][4 * run + e] += kLog2e * static_cast<float>(p[3 - e]);
+      }
+      continue;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (k0 + e < T) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int idx = (rp.qr[qb] - kr + rp.H - 1) * (2 * rp.W - 1) + (rp.qc[qb] - kc + rp.W - 1);
-          s[qb][4 * run + e] += kLog2e * static_cast<float>(rp.tab[int64_t(idx) * rp.n]);
+          const bf16 t = REL == 2 ? rp.slice[idx - rp.lo] : rp.tab[int64_t(idx) * rp.n];
+          s[qb][4 * run + e] += kLog2e * static_cast<float>(t);
         }
       }
       if (++kc == rp.W) {
@@ -292,12 +328,12 @@ __device__ __forceinline__ void add_rel(f32x16 (&s)[QB], const RelPos<QB>& rp, i
   }
 }
 
-template <int D, int QB, int KT, bool MASK, bool REL>
+template <int D, int QB, int KT, bool MASK, int REL>
 __device__ __forceinline__ bool softmax_block(AttnState<D, QB>& st, f32x16 (&s)[QB],
                                               bf16x8 (&pb)[QB][2], float (&delta)[QB], int kb,
                                               int kbase, int T, int half, bool first,
                                               const RelPos<QB>& rp) {
-  if constexpr (REL) add_rel<QB>(s, rp, kbase + kb * 32, T, half);
+  if constexpr (REL != 0) add_rel<QB, REL>(s, rp, kbase + kb * 32, T, half);
   if constexpr (MASK) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -351,7 +387,7 @@ __device__ __forceinline__ bool softmax_block(AttnState<D, QB>& st, f32x16 (&s)[
 // fragments those MFMAs need were read during step kb-1, and step kb reads
 // the fragments of step kb+1 (K of kb+2, V of kb).  When the softmax raises
 // m, the scores of kb+1 (formed against the old m) are shifted by the raise.
-template <int D, int QB, int KT, bool MASK, bool REL>
+template <int D, int QB, int KT, bool MASK, int REL>
 __device__ __forceinline__ void attend_tile(AttnState<D, QB>& st, const bf16* buf, int k0,
                                             int T, int half, int col, bool first,
                                             const RelPos<QB>& rp) {
@@ -485,10 +521,11 @@ constexpr int attn_min_blocks() { return D <= 64 ? 3 : 2; }
 // 256 queries per work-group, used for short sequences (T <= 256, one
 // work-group per (sample, head)) so that K and V are read once per head.
 // (The relative-position variant needs a few more registers: two work-groups per CU.)
-template <int D, int QB, int KT, int NW, bool REL>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? (REL ? 2 : attn_min_blocks<D>()) : 1) void attn_bf16_kernel(AttnParams ap) {
+template <int D, int QB, int KT, int NW, int REL>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<D>()) : 1) void attn_bf16_kernel(AttnParams ap) {
   typedef Tile<D, QB, KT, NW> TL;
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF];
+  __shared__ bf16 rel_lds[REL == 2 ? 2 * kRelSlice : 1];  // table slices of two key tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -506,7 +543,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL ? 2 : attn_min_blocks<D>())
   AttnState<D, QB> st;
   init_state<D, QB>(st, Q, qtile * TL::QT + wave * TL::QPW, T, half, col);
   RelPos<QB> rp;
-  if constexpr (REL) {
+  if constexpr (REL != 0) {
     rp.tab = static_cast<const bf16*>(ap.rel) + head;
     rp.H = ap.H;
     rp.W = ap.W;
@@ -521,12 +558,51 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL ? 2 : attn_min_blocks<D>())
 
   const int ntiles = (T + KT - 1) / KT;
   const int nfull = T / KT;
+  // REL = 2: the table slice of key tile j travels with the tile (loaded with
+  // the tile's prefetch, written to rel_lds slot j&1 with it).
+  constexpr int RPT = REL == 2 ? kRelSlice / TL::NTHR : 1;  // slice entries per thread
+  bf16 rel_pf[RPT];
+  auto q_range = [&](int& q0, int& q1) {
+    q0 = qtile * TL::QT;
+    q1 = min(q0 + TL::QT, T) - 1;
+  };
+  auto rel_load = [&](int k0) {
+    if constexpr (REL == 2) {
+      int q0, q1, lo, len;
+      q_range(q0, q1);
+      rel_rows(q0, q1, k0, min(k0 + KT, T) - 1, ap.H, ap.W, lo, len);
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        const int i = tid + TL::NTHR * u;
+        rel_pf[u] = i < len ? rp.tab[int64_t(lo + i) * ap.n] : bf16(0.f);
+      }
+    }
+  };
+  auto rel_store = [&](int slot) {
+    if constexpr (REL == 2) {
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) rel_lds[slot * kRelSlice + tid + TL::NTHR * u] = rel_pf[u];
+    }
+  };
+  auto rel_use = [&](int j) {  // the slice of tile j (its LDS slot and first row)
+    if constexpr (REL == 2) {
+      int q0, q1, len;
+      q_range(q0, q1);
+      rel_rows(q0, q1, j * KT, min(j * KT + KT, T) - 1, ap.H, ap.W, rp.lo, len);
+      rp.slice = rel_lds + (j & 1) * kRelSlice;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        rp.qrow[qb] = (rp.qr[qb] + ap.H - 1) * (2 * ap.W - 1) + rp.qc[qb] + ap.W - 1 - rp.lo;
+    }
+  };
   Prefetch<D, QB, KT, NW> pf;
   if (nfull > 0)
     load_tile<D, QB, KT, NW, false>(pf, K, Vt, ap.Tp, 0, T, tid);
   else
     load_tile<D, QB, KT, NW, true>(pf, K, Vt, ap.Tp, 0, T, tid);
+  rel_load(0);
   store_tile<D, QB, KT, NW>(lds, pf, tid);
+  rel_store(0);
 
   for (int j = 0; j < nfull; ++j) {
     __syncthreads();  // tile j is in buffer j&1; buffer (j+1)&1 is free
@@ -535,12 +611,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL ? 2 : attn_min_blocks<D>())
       load_tile<D, QB, KT, NW, false>(pf, K, Vt, ap.Tp, kn, T, tid);
     else if (j + 1 < ntiles)
       load_tile<D, QB, KT, NW, true>(pf, K, Vt, ap.Tp, kn, T, tid);
+    if (j + 1 < ntiles) rel_load(kn);
+    rel_use(j);
     attend_tile<D, QB, KT, false, REL>(st, lds + (j & 1) * TL::BUF, j * KT, T, half, col, j == 0,
                                        rp);
-    if (j + 1 < ntiles) store_tile<D, QB, KT, NW>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
+    if (j + 1 < ntiles) {
+      store_tile<D, QB, KT, NW>(lds + ((j + 1) & 1) * TL::BUF, pf, tid);
+      rel_store((j + 1) & 1);
+    }
   }
   if (nfull < ntiles) {  // the partial last tile
     __syncthreads();
+    rel_use(nfull);
     attend_tile<D, QB, KT, true, REL>(st, lds + (nfull & 1) * TL::BUF, nfull * KT, T, half, col,
                                       nfull == 0, rp);
   }
@@ -642,20 +724,30 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams ap) {
   }
 }
 
-template <int D, int QB, int KT, int NW, bool REL>
+template <int D, int QB, int KT, int NW, int REL>
 void launch_bf16_v(AttnParams ap, int64_t bh, hipStream_t stream) {
   typedef Tile<D, QB, KT, NW> TL;
   ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
   attn_bf16_kernel<D, QB, KT, NW, REL><<<dim3(unsigned(bh * ap.qtiles)), TL::NTHR, 0, stream>>>(ap);
 }
 
-// The relative-position variant comes in the 4-wave shape only.
+// The relative-position variant comes in the 4-wave shape only.  Its table
+// slices go through LDS when every (query tile, key tile) pair's slice fits
+// kRelSlice entries: a query tile spans at most ceil((QT-1)/W) + 1 grid rows
+// and a key tile ceil((KT-1)/W) + 1, and a slice covers (row spans - 1 + 1)
+// blocks of 2W - 1 rows.
 template <int D, int QB, int KT, int NW>
 void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
-  if (ap.rel != nullptr)
-    launch_bf16_v<D, QB, KT, 4, true>(ap, bh, stream);
-  else
-    launch_bf16_v<D, QB, KT, NW, false>(ap, bh, stream);
+  if (ap.rel != nullptr) {
+    typedef Tile<D, QB, KT, 4> TL;
+    const int64_t spans = (TL::QT - 1 + ap.W - 1) / ap.W + (KT - 1 + ap.W - 1) / ap.W + 1;
+    if (spans * (2 * int64_t(ap.W) - 1) <= kRelSlice)
+      launch_bf16_v<D, QB, KT, 4, 2>(ap, bh, stream);
+    else
+      launch_bf16_v<D, QB, KT, 4, 1>(ap, bh, stream);
+  } else {
+    launch_bf16_v<D, QB, KT, NW, 0>(ap, bh, stream);
+  }
 }
 
 }  // namespace

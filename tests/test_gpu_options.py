@@ -97,6 +97,19 @@ def test_options(wl, flags, stress):
     assert e <= TOL[wl.dtype]
 
 
+# A wide image: a key tile's slice of the relative-position table exceeds the
+# LDS slice buffer, so the attention kernel gathers the bias from the table in
+# global memory (the narrow images above take the LDS slices).
+@pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
+def test_relpos_wide_image(stress):
+    wl = Workload("bf16 d64 2x300", "bf16", 1, 128, 2, 300, 8, 2)
+    x, p, opts, out = run_case(wl, 52, stress, rel_pos=True)
+    want = ORA.forward(*to_f64(x, p), wl.num_groups, wl.num_heads, **options_f64(opts))
+    e = err(out.double().cpu().numpy(), want, wl.dtype)
+    print(f"  err {e:.3e}", flush=True)
+    assert e <= TOL[wl.dtype]
+
+
 @pytest.mark.parametrize("idx", [1, 3])
 def test_options_full_size_sampled(idx):
     wl = WORKLOADS[idx]
