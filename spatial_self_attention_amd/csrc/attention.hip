@@ -267,12 +267,16 @@ struct RelPos {
   const bf16* tab;   // table + head
   int H, W, n;
   int qr[QB], qc[QB];
-  const bf16* slice;  // REL = 2: LDS copy of table rows lo .. of this head
+  const float* slice;  // REL = 2: table rows lo .. of this head times log2(e), fp32 (LDS)
   int lo;
-  int qrow[QB];       // REL = 2: (row(q) + H - 1)(2W - 1) + col(q) + W - 1 - lo
+  int qrow[QB];        // REL = 2: (row(q) + H - 1)(2W - 1) + col(q) + W - 1 - lo
+  const int* kterm;    // REL = 2: row(k)(2W - 1) + col(k) of the tile's keys (LDS)
+  int k0;              // REL = 2: the tile's first key
 };
 
-// Entries of the table slice one work-group stages per key tile (REL = 2).
+// Entries of the table slice one work-group stages per key tile (REL = 2),
+// kept in LDS as fp32 already multiplied by log2(e): a score then takes one
+// LDS read and one add.
 constexpr int kRelSlice = 1024;
 
 // Table rows (first, count) that queries q0..q1 meet against keys k0..k1.
@@ -293,36 +297,37 @@ __device__ __forceinline__ void rel_rows(int q0, int q1, int k0, int k1, int H, 
 template <int QB, int REL>
 __device__ __forceinline__ void add_rel(f32x16 (&s)[QB], const RelPos<QB>& rp, int kfirst, int T,
                                         int half) {
+  if constexpr (REL == 2) {
+    // table row of (q, k) = qrow(q) + lo - kterm(k): a run's four key terms
+    // come in one 16-byte LDS read, each score's entry in one more
 #pragma unroll
-  for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
-    const int k0 = kfirst + 8 * run + 4 * half;
-    int kr = k0 / rp.W, kc = k0 - kr * rp.W;
-    if (REL == 2 && kc + 3 < rp.W && k0 + 3 < T) {
-      // four keys in one grid row: their table rows are consecutive (row(q) -
-      // row(k) fixed, col(k) + e), i.e. four adjacent slice entries, read
-      // backwards from one address
-      const int kterm = kr * (2 * rp.W - 1) + kc;
+    for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
+      const int kk = kfirst - rp.k0 + 8 * run + 4 * half;
+      const int4 kt = *reinterpret_cast<const int4*>(rp.kterm + kk);
+      const int kte[4] = {kt.x, kt.y, kt.z, kt.w};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const bf16* p = rp.slice + (rp.qrow[qb] - kterm - 3);
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[qb][4 * run + e] += kLog2e * static_cast<float>(p[3 - e]);
-      }
-      continue;
+        for (int e = 0; e < 4; ++e) s[qb][4 * run + e] += rp.slice[rp.qrow[qb] - kte[e]];
     }
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (k0 + e < T) {
+    for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
+      const int k0 = kfirst + 8 * run + 4 * half;
+      int kr = k0 / rp.W, kc = k0 - kr * rp.W;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int idx = (rp.qr[qb] - kr + rp.H - 1) * (2 * rp.W - 1) + (rp.qc[qb] - kc + rp.W - 1);
-          const bf16 t = REL == 2 ? rp.slice[idx - rp.lo] : rp.tab[int64_t(idx) * rp.n];
-          s[qb][4 * run + e] += kLog2e * static_cast<float>(t);
+      for (int e = 0; e < 4; ++e) {
+        if (k0 + e < T) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int idx = (rp.qr[qb] - kr + rp.H - 1) * (2 * rp.W - 1) + (rp.qc[qb] - kc + rp.W - 1);
+            s[qb][4 * run + e] += kLog2e * static_cast<float>(rp.tab[int64_t(idx) * rp.n]);
+          }
         }
-      }
-      if (++kc == rp.W) {
-        kc = 0;
-        ++kr;
+        if (++kc == rp.W) {
+          kc = 0;
+          ++kr;
+        }
       }
     }
   }
@@ -525,7 +530,8 @@ template <int D, int QB, int KT, int NW, int REL>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<D>()) : 1) void attn_bf16_kernel(AttnParams ap) {
   typedef Tile<D, QB, KT, NW> TL;
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF];
-  __shared__ bf16 rel_lds[REL == 2 ? 2 * kRelSlice : 1];  // table slices of two key tiles
+  __shared__ float rel_lds[REL == 2 ? 2 * kRelSlice : 1];  // table slices of two key tiles
+  __shared__ __attribute__((aligned(16))) int kterm_lds[REL == 2 ? 2 * KT : 1];  // their key terms
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -561,7 +567,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<
   // REL = 2: the table slice of key tile j travels with the tile (loaded with
   // the tile's prefetch, written to rel_lds slot j&1 with it).
   constexpr int RPT = REL == 2 ? kRelSlice / TL::NTHR : 1;  // slice entries per thread
-  bf16 rel_pf[RPT];
+  float rel_pf[RPT];
+  int kterm_pf = 0;  // key term of key k0 + tid (tid < KT); keys past T take key T-1's
   auto q_range = [&](int& q0, int& q1) {
     q0 = qtile * TL::QT;
     q1 = min(q0 + TL::QT, T) - 1;
@@ -574,14 +581,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
         const int i = tid + TL::NTHR * u;
-        rel_pf[u] = i < len ? rp.tab[int64_t(lo + i) * ap.n] : bf16(0.f);
+        rel_pf[u] = i < len ? kLog2e * static_cast<float>(rp.tab[int64_t(lo + i) * ap.n]) : 0.f;
       }
+      const int key = min(k0 + tid, T - 1);
+      const int kr = key / ap.W;
+      kterm_pf = kr * (2 * ap.W - 1) + (key - kr * ap.W);
     }
   };
   auto rel_store = [&](int slot) {
     if constexpr (REL == 2) {
 #pragma unroll
       for (int u = 0; u < RPT; ++u) rel_lds[slot * kRelSlice + tid + TL::NTHR * u] = rel_pf[u];
+      if (tid < KT) kterm_lds[slot * KT + tid] = kterm_pf;
     }
   };
   auto rel_use = [&](int j) {  // the slice of tile j (its LDS slot and first row)
@@ -590,6 +601,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<
       q_range(q0, q1);
       rel_rows(q0, q1, j * KT, min(j * KT + KT, T) - 1, ap.H, ap.W, rp.lo, len);
       rp.slice = rel_lds + (j & 1) * kRelSlice;
+      rp.kterm = kterm_lds + (j & 1) * KT;
+      rp.k0 = j * KT;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         rp.qrow[qb] = (rp.qr[qb] + ap.H - 1) * (2 * ap.W - 1) + rp.qc[qb] + ap.W - 1 - rp.lo;
