@@ -9,9 +9,14 @@
 //    the float32 construction the page describes.
 // Normalisation comes first, then the rotation (which keeps norms).
 //
-// One group of P lanes (P a power of two >= ceil(d/2)) owns one (token, head)
-// row; lane i holds elements i and i + ceil(d/2).  The squared norm is summed
-// over the group with lane shuffles.  The bf16 queries arrive multiplied by
+// General kernel: one group of P lanes (P a power of two >= ceil(d/2)) owns
+// one (token, head) row; lane i holds elements i and i + ceil(d/2).  The
+// squared norm is summed over the group with lane shuffles.
+// bf16 kernel for d % 8 == 0: one group of P lanes owns one (sample, token)
+// and walks the 2n rows of Q and K that share it (every head), lane j holding
+// elements 4j..4j+3 and d/2 + 4j..4j+3 as 8-byte vectors; the rotation's
+// sines and cosines depend only on (token, element), so a lane forms its four
+// once for all 2n rows.  The bf16 queries arrive multiplied by
 // log2(e)/sqrt(d) (the attention kernel's score scale): normalisation removes
 // that factor, so normalised bf16 queries are multiplied by log2(e) (scores in
 // the log2 domain, no 1/sqrt(d)); the rotation is linear and keeps it.
@@ -72,6 +77,77 @@ __global__ __launch_bounds__(256) void qk_post_kernel(QkPostParams pp) {
   if (hb) base[i + hd] = from_f32<T>(b);
 }
 
+template <int P>
+__global__ __launch_bounds__(256) void qk_post_bf16_kernel(QkPostParams pp) {
+  const int tid = threadIdx.x;
+  const int j = tid % P;                          // this lane's element chunk
+  const int item = blockIdx.x * (256 / P) + tid / P;  // (b, t)
+  const int hd = pp.hd, d = pp.d, n = pp.n, T = pp.T;
+  const int nitems = pp.rows / n;                 // B * T
+  if (item >= nitems) return;                     // whole groups leave together
+  const bool act = 4 * j < hd;
+  const int b = item / T, t = item - b * T;
+  const int i = act ? 4 * j : 0;
+  float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+  if (pp.rope) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sincosf(float(t) * pp.theta[i + e], &sn[e], &cs[e]);
+  }
+  const bf16* gq = static_cast<const bf16*>(pp.gq);
+  const bf16* gk = static_cast<const bf16*>(pp.gk);
+  for (int r = 0; r < 2 * n; ++r) {
+    const bool isq = r < n;
+    const int head = isq ? r : r - n;
+    bf16* base = static_cast<bf16*>(isq ? pp.q : pp.k) + ((int64_t(b) * n + head) * T + t) * d;
+    bf16x4 va = {}, vb = {};
+    if (act) {
+      va = *reinterpret_cast<const bf16x4*>(base + i);
+      vb = *reinterpret_cast<const bf16x4*>(base + hd + i);
+    }
+    float a[4], c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = static_cast<float>(va[e]);
+      c[e] = static_cast<float>(vb[e]);
+    }
+    if (gq != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + c[e] * c[e];
+#pragma unroll
+      for (int m = P / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, P);
+      const float f = sqrtf(float(d)) / fmaxf(sqrtf(ss), 1e-12f) * (isq ? pp.qmul : 1.f);
+      if (act) {
+        const bf16* g = (isq ? gq : gk) + head * d;
+        const bf16x4 ga = *reinterpret_cast<const bf16x4*>(g + i);
+        const bf16x4 gb = *reinterpret_cast<const bf16x4*>(g + hd + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] *= f * static_cast<float>(ga[e]);
+          c[e] *= f * static_cast<float>(gb[e]);
+        }
+      }
+    }
+    if (pp.rope) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float na = a[e] * cs[e] - c[e] * sn[e], nc = c[e] * cs[e] + a[e] * sn[e];
+        a[e] = na;
+        c[e] = nc;
+      }
+    }
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        va[e] = static_cast<bf16>(a[e]);
+        vb[e] = static_cast<bf16>(c[e]);
+      }
+      *reinterpret_cast<bf16x4*>(base + i) = va;
+      *reinterpret_cast<bf16x4*>(base + hd + i) = vb;
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const QkPostParams& pp, hipStream_t stream) {
   const int hd = pp.hd;
@@ -106,6 +182,18 @@ hipError_t launch_qk_post(const Plan& p, const Args& a) {
   pp.qmul = p.dtype == SSA_BF16 ? 1.4426950408889634f : 1.f;
   for (int i = 0; i < pp.hd && i < kMaxHalf; ++i)
     pp.theta[i] = float(pow(10000.0, -2.0 * double(i) / double(p.d)));
+  if (p.dtype == SSA_BF16 && p.d % 8 == 0) {
+    const int chunks = pp.hd / 4;  // 4, 8, 12 or 16
+    const int P = chunks <= 4 ? 4 : chunks <= 8 ? 8 : 16;
+    const int64_t items = p.B * p.T;
+    const unsigned grid = unsigned((items * P + 255) / 256);
+    switch (P) {
+      case 4: qk_post_bf16_kernel<4><<<grid, 256, 0, a.stream>>>(pp); break;
+      case 8: qk_post_bf16_kernel<8><<<grid, 256, 0, a.stream>>>(pp); break;
+      default: qk_post_bf16_kernel<16><<<grid, 256, 0, a.stream>>>(pp); break;
+    }
+    return hipGetLastError();
+  }
   return p.dtype == SSA_F32 ? launch_typed<float>(pp, a.stream) : launch_typed<bf16>(pp, a.stream);
 }
 
