@@ -470,8 +470,8 @@ __device__ __forceinline__ const bf16* row_bias(const ProjParams& pp, int which)
   return static_cast<const bf16*>(which == 0 ? pp.bias[0] : which == 1 ? pp.bias[1] : pp.bias[2]);
 }
 
-// Residual run u of a lane (output projection): channel row ec.mw + 4u + (lane >> 4)
-// of sample b, tokens t .. t+3 of this lane's run; byte offsets into x.
+// The sample b and token t of this lane's run of 4 tokens in the V^T and
+// output epilogues (lane & 15 picks the run); false past the last token.
 __device__ __forceinline__ bool res_run(const ProjParams& pp, const EpiCtx& ec, int& b, int& t) {
   const int nn = ec.nw + 4 * (ec.lane & 15);
   if (nn >= pp.NT) return false;  // NT % 4 == 0: a run is all in or all out
