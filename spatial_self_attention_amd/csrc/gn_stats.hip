@@ -17,6 +17,7 @@
 //       (count, mean, M2) and
 //   gn_finalize_kernel      grid B*G: one wave merges the chunks of a segment
 //       and emits the same statistics and coefficients.
+//   gn_stats_wave_kernel    many short segments: one wave per segment.
 #include "ssa_internal.h"
 
 namespace ssa {
@@ -151,6 +152,57 @@ __global__ __launch_bounds__(256) void gn_stats_kernel(const T* __restrict__ x,
   }
 }
 
+// Many short segments (at most kWaveSeg elements, at least four per CU): one
+// wave per segment, four per work-group, every load of a lane issued before
+// the sums; the merge is the wave's alone (no LDS, no barrier).  A quarter of
+// the work-groups of one-per-segment, which matters when the segments are
+// small and the launch is mostly latency.
+constexpr int kWaveSeg = 4096;
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void gn_stats_wave_kernel(const T* __restrict__ x, int64_t segs,
+                                                            int seg_len,
+                                                            const T* __restrict__ gamma,
+                                                            const T* __restrict__ beta,
+                                                            float2* __restrict__ stats,
+                                                            float2* __restrict__ coef, int G,
+                                                            int Cg, int C) {
+  typedef typename VecOf<T, VEC>::type V;
+  constexpr int NV = kWaveSeg / VEC / 64;  // vectors per lane at most
+  const int lane = threadIdx.x & 63;
+  const int64_t seg = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (seg >= segs) return;  // whole waves
+  const V* vb = reinterpret_cast<const V*>(x + seg * seg_len);
+  const int nv = seg_len / VEC;
+  const float x0 = to_f32(x[seg * seg_len]);
+  V v[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    if (lane + 64 * u < nv) v[u] = vb[lane + 64 * u];
+  float sd = 0.f, sq = 0.f;
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    if (lane + 64 * u < nv) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float d = to_f32(v[u][e]) - x0;
+        sd += d;
+        sq = fmaf(d, d, sq);
+      }
+      cnt += VEC;
+    }
+  }
+  Moments acc{0.f, 0.f, 0.f};
+  if (cnt > 0) {
+    const float n = float(cnt);
+    const float md = sd / n;
+    acc = Moments{n, x0 + md, fmaxf(sq - sd * md, 0.f)};
+  }
+  acc = wave_merge(acc);
+  finalize<T>(acc, int(seg), gamma, beta, stats, coef, G, Cg, C, lane, 64);
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void gn_finalize_kernel(const float4* __restrict__ partial,
                                                          int splits, const T* __restrict__ gamma,
@@ -179,6 +231,14 @@ hipError_t launch_vec(const Plan& p, const Args& a) {
   const T* beta = static_cast<const T*>(a.norm_bias);
   const int G = int(p.G), Cg = int(p.C / p.G), C = int(p.C);
   dim3 grid(unsigned(p.splits * p.B * p.G));
+  if constexpr (VEC > 1) {
+    if (p.splits == 1 && p.seg_len <= kWaveSeg && p.B * p.G >= 4 * int64_t(p.cus)) {
+      const int64_t segs = p.B * p.G;
+      gn_stats_wave_kernel<T, VEC><<<dim3(unsigned((segs + 3) / 4)), 256, 0, a.stream>>>(
+          x, segs, int(p.seg_len), gamma, beta, stats, coef, G, Cg, C);
+      return hipGetLastError();
+    }
+  }
   if (p.splits == 1) {
     gn_stats_kernel<T, VEC, true><<<grid, 256, 0, a.stream>>>(x, partial, p.seg_len, p.chunk, 1,
                                                               gamma, beta, stats, coef, G, Cg, C);

@@ -204,6 +204,29 @@ def test_full_size_sampled(idx, stress):
     assert worst <= TOL[wl.dtype]
 
 
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_gn_statistics_full_size(idx):
+    """GroupNorm statistics and coefficients of every (b, g) at the full
+    workload sizes, one for each statistics launch shape: one wave per segment
+    (workload 1: 2048 short segments), one work-group per segment with the
+    finalise fused (workload 2), split segments merged by a second kernel
+    (workloads 3 and 4)."""
+    wl = WORKLOADS[idx]
+    x, p, _, ws = run(wl, 1100 + idx)
+    x64, p64 = to_f64(x, p)
+    _, mean, var = ORA.group_norm(x64, p64["norm_weight"], p64["norm_bias"], wl.num_groups)
+    rstd = 1.0 / np.sqrt(var + 1e-5)
+    stats, _ = region(ws, wl, "gn_stats", torch.float32, (wl.B, wl.num_groups, 2))
+    assert np.max(np.abs(stats[..., 0] - mean)) <= 1e-5 * (1 + np.max(np.abs(mean)))
+    assert np.max(np.abs(stats[..., 1] / rstd - 1)) <= 1e-5
+    coef, _ = region(ws, wl, "gn_coef", torch.float32, (wl.B, wl.C, 2))
+    Cg = wl.C // wl.num_groups
+    a = p64["norm_weight"][None] * np.repeat(rstd, Cg, axis=1)
+    s_ = p64["norm_bias"][None] - np.repeat(mean, Cg, axis=1) * a
+    assert np.max(np.abs(coef[..., 0] - a)) <= 1e-5 * np.max(np.abs(a))
+    assert np.max(np.abs(coef[..., 1] - s_)) <= 1e-5 * (1 + np.max(np.abs(a)))
+
+
 def test_largest_accepted_call():
     """The largest size the library accepts, 3*B*T*C just below 2^31: x, out
     and each of Q, K, V^T, O hold 7.2e8 bf16 elements (1.43e9 bytes, the
