@@ -378,6 +378,13 @@ __device__ __forceinline__ void gemm_load(Stage& sg, const LoadCtx& lc, int k0) 
   }
 }
 
+// LDS row of token t in the QKV projection's B tile.  A thread writes rows
+// tq*4 + u of four token quads per 8-lane group, which with 144-byte rows puts
+// two lanes on the same banks; flipping bit 1 of the row when bit 3 is set
+// spreads those writes over 8 bank groups and keeps the fragment reads (8
+// consecutive tokens) on 8 distinct groups as well.
+__device__ __forceinline__ int brow(int t) { return t ^ ((t >> 2) & 2); }
+
 // Part u (0..3) of writing a register stage to LDS: A vector u (row
 // (tid >> 3) + 32u) and, for the output projection, B vector u (token row
 // (tid >> 3) + 32u of O); for Q/K/V token tq*4 + u of the thread's quad,
@@ -398,7 +405,7 @@ __device__ __forceinline__ void store_part(bf16* As, bf16* Bs, const Stage& sg, 
       z[j] = static_cast<bf16>(fmaf(a, xv, sh));
     }
     const int tq = qkv_tq(tid), co = qkv_co(tid);
-    *reinterpret_cast<bf16x8*>(&Bs[(tq * 4 + u) * GP + co * 8]) = z;
+    *reinterpret_cast<bf16x8*>(&Bs[brow(tq * 4 + u) * GP + co * 8]) = z;
   }
 }
 
@@ -413,15 +420,17 @@ struct Frags {
   bf16x8 a[2], b[2];
 };
 
+template <int MODE>
 __device__ __forceinline__ void read_frags(Frags& f, const bf16* As, const bf16* Bs, int wm,
                                            int wn, int half, int col, int s) {
   const int kofs = s * 16 + half * 8;
+  const int bcol = MODE == kQkv ? brow(col) : col;  // rows wn*64 + j*32 keep bits 1 and 3 clear
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     f.a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + col) * GP + kofs]);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + col) * GP + kofs]);
+    f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 32 + bcol) * GP + kofs]);
 }
 
 // The 2 x 2 MFMAs of one sub-step.
@@ -558,13 +567,13 @@ __device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], EpiPre& ep, const
     // u's MFMAs.
     constexpr bool kAhead = MODE == kOut;
     Frags f[2];
-    if (kAhead) read_frags(f[0], rd, rd + GM * GP, wm, wn, half, col, 0);
+    if (kAhead) read_frags<MODE>(f[0], rd, rd + GM * GP, wm, wn, half, col, 0);
 #pragma unroll
     for (int u = 0; u < GK / 16; ++u) {
       if (kAhead) {
-        if (u + 1 < GK / 16) read_frags(f[(u + 1) & 1], rd, rd + GM * GP, wm, wn, half, col, u + 1);
+        if (u + 1 < GK / 16) read_frags<MODE>(f[(u + 1) & 1], rd, rd + GM * GP, wm, wn, half, col, u + 1);
       } else {
-        read_frags(f[u & 1], rd, rd + GM * GP, wm, wn, half, col, u);
+        read_frags<MODE>(f[u & 1], rd, rd + GM * GP, wm, wn, half, col, u);
       }
       mfma_sub<TR>(acc, f[u & 1]);
       if (more) store_part<MODE>(wr, wr + GM * GP, nxt, tid, u);
