@@ -98,10 +98,12 @@ def cpu_baseline(wl, seed, budget_s=12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    # whole samples of the batch in order, passing over the batch again while the
+    # time budget lasts (a small batch alone would be too short to time)
     one = wl.replace(B=1)
     done, flops, el = 0, 0, 0.0
-    while done < wl.B and el < budget_s:
-        x64, p64 = to_f64(*draw(one, seed + done))
+    while el < budget_s:
+        x64, p64 = to_f64(*draw(one, seed + done % wl.B))
         t1 = time.perf_counter()
         oracle_forward(x64, p64, wl.num_groups, wl.num_heads)
         el += time.perf_counter() - t1
@@ -109,8 +111,9 @@ def cpu_baseline(wl, seed, budget_s=12.0):
         flops += one.flops()
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {wl.B} samples of {wl.name}, one whole sample per oracle "
-                      f"call, fp64 NumPy, {el:.1f} s of oracle time",
+            "sample": f"{done} oracle calls over the {wl.B} samples of {wl.name} "
+                      f"({done / wl.B:.2f} passes), one whole sample per call, fp64 NumPy, "
+                      f"{el:.1f} s of oracle time",
             "pixels_per_s": done * wl.T / el}
 
 

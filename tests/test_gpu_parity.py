@@ -68,6 +68,9 @@ STAGE_CASES = [
     WORKLOADS[3].replace(B=1, H=24, W=40),
     WORKLOADS[4].replace(B=1, H=20, W=23),
     Workload("fp32 ragged", "f32", 2, 96, 5, 7, 4, 3),
+    # a large batch of small images: 3120 QKV and 1040 output-projection tiles,
+    # several rounds of work-groups on a 256-CU chip
+    Workload("many samples", "bf16", 520, 128, 16, 16, 8, 2),
 ]
 
 
