@@ -4,15 +4,16 @@
                     [--options relpos,qknorm,rope]
 
 A step is one ssa_forward over one batch of the selected workload (GroupNorm
-statistics, QKV projection, flash attention, output projection + residual),
-with inputs already resident in HBM.  W untimed steps, then exactly K steps
+statistics, QKV projection, flash attention, output projection + residual;
+where the library fuses them, projection and attention are one kernel), with
+inputs already resident in HBM.  W untimed steps, then exactly K steps
 between two device synchronisations; the value is block TFLOP/s
 (8BTC^2 + 4BT^2C flops per step).  Prints one JSON line.
 
 Also reported:
 * per-kernel average durations from HIP events on the launch stream, each
-  stage replayed back-to-back from a HIP graph so host launch overhead is not
-  counted; the dominant kernel's roofline (algorithmic flops or bytes per
+  stage the step runs replayed back-to-back from a HIP graph so host launch
+  overhead is not counted; the dominant kernel's roofline (algorithmic flops or bytes per
   launch over its average duration, against MI355X's dense bf16 MFMA peak or
   HBM bandwidth), with HBM traffic from the stored rocprofv3 counter summary
   when it was taken on the current kernel sources;
@@ -61,6 +62,7 @@ def stage_work(wl):
         "gn_stats": ("bytes", B * C * T * es),
         "qkv": ("flops", 6 * B * T * C * C),
         "attention": ("flops", 4 * B * T * T * C),
+        "qkv_attention": ("flops", 6 * B * T * C * C + 4 * B * T * T * C),
         "out_proj": ("flops", 2 * B * T * C * C),
     }
 
@@ -70,6 +72,7 @@ STAGE_KERNELS = {
     "gn_stats": "gn_stats_kernel (+ gn_finalize_kernel when segments are split)",
     "qkv": "gemm_bf16_kernel<0>",
     "attention": "attn_bf16_kernel",
+    "qkv_attention": "fused_bf16_kernel",
     "out_proj": "gemm_bf16_kernel<1>",
 }
 
@@ -220,7 +223,8 @@ def main():
     # ---- per-kernel durations: each stage replayed back-to-back from a graph ----
     reps = max(20, min(args.steps, 200))
     per_stage = {}
-    for stage in ("gn_stats", "qkv", "attention", "out_proj"):
+    stages = ssa.forward_stages(xg, wl.num_groups, wl.num_heads)
+    for stage in stages:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(reps):
@@ -240,7 +244,7 @@ def main():
     torch.cuda.synchronize()
 
     work = stage_work(wl)
-    dom = max(("qkv", "attention", "out_proj"), key=lambda s: per_stage[s])
+    dom = max((s for s in stages if s != "gn_stats"), key=lambda s: per_stage[s])
     kind, amount = work[dom]
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = amount / per_stage[dom] / 1e12

@@ -85,12 +85,16 @@ typedef enum {
 
 typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
 
-/* The four kernels of the block, in launch order. */
+/* The kernels of the block.  ssa_forward runs stages 0, 1, 2, 3 in this
+ * order, or 0, 4, 3 where ssa_uses_fused_stage() returns 1 (then q, k and vt
+ * of the workspace are not written). */
 typedef enum {
   SSA_STAGE_GN_STATS = 0,   /* GroupNorm statistics -> gn_stats, gn_coef        */
   SSA_STAGE_QKV = 1,        /* normalise + Q/K/V projections -> q, k, vt        */
   SSA_STAGE_ATTENTION = 2,  /* per-head softmax(QK^T/sqrt(d))V -> o             */
-  SSA_STAGE_OUT_PROJ = 3    /* o Wo^T + bo + x, back to NCHW -> out             */
+  SSA_STAGE_OUT_PROJ = 3,   /* o Wo^T + bo + x, back to NCHW -> out             */
+  SSA_STAGE_QKV_ATTENTION = 4 /* stages 1 and 2 in one kernel -> o (the same
+                                 bits); reads gn_coef, writes only o          */
 } ssa_stage;
 
 typedef struct {
@@ -131,11 +135,13 @@ ssa_status ssa_forward(const void* x, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of the block, with the same arguments and validation as
- * ssa_forward.  Running stages 0, 1, 2, 3 in order on one stream with one
- * workspace is exactly ssa_forward.  A stage reads what the earlier stages
- * left in the workspace; running it out of order computes from whatever the
- * workspace holds (no error is detectable).  Used to time and inspect each
- * kernel separately. */
+ * ssa_forward.  Running stages 0, 1, 2, 3 (or, where the fused stage is
+ * available, 0, 4, 3) in order on one stream with one workspace is exactly
+ * ssa_forward; both orders give the same output bit for bit.  A stage reads
+ * what the earlier stages left in the workspace; running it out of order
+ * computes from whatever the workspace holds (no error is detectable).
+ * Stage 4 returns SSA_E_UNSUPPORTED for sizes ssa_uses_fused_stage() rejects.
+ * Used to time and inspect each kernel separately. */
 ssa_status ssa_forward_stage(int stage,
                              const void* x, void* out,
                              const void* norm_weight, const void* norm_bias,
@@ -187,6 +193,16 @@ ssa_status ssa_forward_ex(const void* x, void* out,
                           int64_t num_groups, int64_t num_heads, int dtype,
                           const ssa_options* options,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* 1 when ssa_forward (and ssa_forward_ex with no optional step on) runs the
+ * fused stage SSA_STAGE_QKV_ATTENTION for this problem, else 0 (also for
+ * arguments ssa_forward would reject).  The fused kernel keeps one head's
+ * Q, K and V in the LDS of one compute unit: bf16, head size 128, 192 < H*W
+ * <= 256 with H*W a multiple of 4, and at least one (sample, head) pair per
+ * compute unit of the current device (tensortonic "Spatial Self-Attention":
+ * the projections and the per-head attention of its formula). */
+int ssa_uses_fused_stage(int64_t B, int64_t C, int64_t H, int64_t W,
+                         int64_t num_groups, int64_t num_heads, int dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* ssa_status_string(int status);

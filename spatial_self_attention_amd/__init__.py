@@ -17,7 +17,7 @@ import torch
 from ._binding import (  # noqa: F401
     BIAS_KEYS, EXPORTS, LIB_PATH, PARAM_ORDER, SSA_BF16, SSA_F32, STAGES, Options, SSAError,
     SSAValueError, lib, ssa_forward, ssa_forward_ex, ssa_forward_stage, ssa_get_workspace_layout,
-    ssa_status_string, ssa_workspace_size,
+    ssa_status_string, ssa_uses_fused_stage, ssa_workspace_size,
 )
 from ._binding import _raise
 
@@ -85,6 +85,14 @@ def make_options(x, num_heads, rel_pos_table=None, q_norm_gamma=None, k_norm_gam
         if t.dtype != x.dtype or t.device != x.device or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous with x's dtype and device")
     return Options(_ptr(rel_pos_table), _ptr(q_norm_gamma), _ptr(k_norm_gamma), 1 if rope else 0)
+
+
+def forward_stages(x, num_groups: int, num_heads: int) -> tuple:
+    """The stage names ssa_forward runs for x's problem, in order."""
+    B, C, H, W = x.shape
+    if ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads, dtype_code(x.dtype)):
+        return ("gn_stats", "qkv_attention", "out_proj")
+    return ("gn_stats", "qkv", "attention", "out_proj")
 
 
 def forward_into(x, params, num_groups, num_heads, out, workspace, stage=None,

@@ -19,7 +19,7 @@ STATUS_NAMES = {
     7: "SSA_E_ALIAS", 8: "SSA_E_ALIGN", 9: "SSA_E_HIP", 10: "SSA_E_STAGE",
 }
 SSA_F32, SSA_BF16 = 0, 1
-STAGES = {"gn_stats": 0, "qkv": 1, "attention": 2, "out_proj": 3}
+STAGES = {"gn_stats": 0, "qkv": 1, "attention": 2, "out_proj": 3, "qkv_attention": 4}
 
 # Parameter order of the ABI (the problem's parameter table).
 PARAM_ORDER = (
@@ -29,7 +29,7 @@ PARAM_ORDER = (
 )
 
 EXPORTS = ("ssa_workspace_size", "ssa_get_workspace_layout", "ssa_forward",
-           "ssa_forward_ex", "ssa_forward_stage", "ssa_status_string")
+           "ssa_forward_ex", "ssa_forward_stage", "ssa_uses_fused_stage", "ssa_status_string")
 
 BIAS_KEYS = ("q_bias", "k_bias", "v_bias", "out_bias")
 
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.ssa_forward_stage.argtypes = [ctypes.c_int] + fwd
     L.ssa_forward_ex.restype = ctypes.c_int
     L.ssa_forward_ex.argtypes = fwd[:19] + [ctypes.POINTER(Options)] + fwd[19:]
+    L.ssa_uses_fused_stage.restype = ctypes.c_int
+    L.ssa_uses_fused_stage.argtypes = [i64] * 6 + [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
     L.ssa_status_string.argtypes = [ctypes.c_int]
     _lib = L
@@ -150,3 +152,8 @@ def ssa_forward_stage(stage, x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups,
     return int(lib().ssa_forward_stage(int(stage), x_ptr, out_ptr, *param_ptrs, B, C, H, W,
                                        num_groups, num_heads, int(dtype), ws_ptr, ws_bytes,
                                        stream_ptr))
+
+
+def ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads, dtype) -> bool:
+    """Whether ssa_forward runs stages 0, 4, 3 (the fused kernel) for this problem."""
+    return bool(lib().ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads, int(dtype)))

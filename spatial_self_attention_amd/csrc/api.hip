@@ -142,7 +142,10 @@ ssa_status check_options(const Plan& p, const Args& a) {
   return SSA_OK;
 }
 
-ssa_status run(int first, int last, const void* x, void* out, const void* nw, const void* nb,
+// stages: the stage codes to enqueue, in order; stage < 0: the whole block
+// (stages 0, 1, 2, 3, or 0, 4, 3 where the fused kernel is available and no
+// optional step is on).
+ssa_status run(int stage, const void* x, void* out, const void* nw, const void* nb,
                const void* qw, const void* kw, const void* vw, const void* ow,
                const void* qb, const void* kb, const void* vb, const void* ob,
                int64_t B, int64_t C, int64_t H, int64_t W, int64_t G, int64_t n, int dtype,
@@ -165,9 +168,21 @@ ssa_status run(int first, int last, const void* x, void* out, const void* nw, co
   if (st != SSA_OK) return st;
   st = check_pointers(p, a, workspace_bytes);
   if (st != SSA_OK) return st;
-  for (int s = first; s <= last; ++s) {
+  const bool plain = a.rel_pos_table == nullptr && a.q_norm_gamma == nullptr && !a.rope;
+  int stages[4] = {SSA_STAGE_GN_STATS, SSA_STAGE_QKV, SSA_STAGE_ATTENTION, SSA_STAGE_OUT_PROJ};
+  int count = 4;
+  if (stage >= 0) {
+    if (stage == SSA_STAGE_QKV_ATTENTION && !fused_available(p)) return SSA_E_UNSUPPORTED;
+    stages[0] = stage;
+    count = 1;
+  } else if (plain && fused_available(p)) {
+    stages[1] = SSA_STAGE_QKV_ATTENTION;
+    stages[2] = SSA_STAGE_OUT_PROJ;
+    count = 3;
+  }
+  for (int i = 0; i < count; ++i) {
     hipError_t e = hipSuccess;
-    switch (s) {
+    switch (stages[i]) {
       case SSA_STAGE_GN_STATS: e = launch_gn_stats(p, a); break;
       case SSA_STAGE_QKV:
         e = launch_qkv_proj(p, a);
@@ -175,6 +190,7 @@ ssa_status run(int first, int last, const void* x, void* out, const void* nw, co
         break;
       case SSA_STAGE_ATTENTION: e = launch_attention(p, a); break;
       case SSA_STAGE_OUT_PROJ: e = launch_out_proj(p, a); break;
+      case SSA_STAGE_QKV_ATTENTION: e = launch_fused(p, a); break;
     }
     if (e != hipSuccess) return SSA_E_HIP;
   }
@@ -213,10 +229,9 @@ ssa_status ssa_forward(const void* x, void* out, const void* norm_weight, const 
                        const void* v_bias, const void* out_bias, int64_t B, int64_t C, int64_t H,
                        int64_t W, int64_t num_groups, int64_t num_heads, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return ssa::run(SSA_STAGE_GN_STATS, SSA_STAGE_OUT_PROJ, x, out, norm_weight, norm_bias,
-                  q_weight, k_weight, v_weight, out_weight, q_bias, k_bias, v_bias, out_bias,
-                  B, C, H, W, num_groups, num_heads, dtype, nullptr, workspace, workspace_bytes,
-                  stream);
+  return ssa::run(-1, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight, out_weight,
+                  q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups, num_heads, dtype,
+                  nullptr, workspace, workspace_bytes, stream);
 }
 
 ssa_status ssa_forward_ex(const void* x, void* out, const void* norm_weight,
@@ -226,10 +241,9 @@ ssa_status ssa_forward_ex(const void* x, void* out, const void* norm_weight,
                           int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
                           int64_t num_heads, int dtype, const ssa_options* options,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return ssa::run(SSA_STAGE_GN_STATS, SSA_STAGE_OUT_PROJ, x, out, norm_weight, norm_bias,
-                  q_weight, k_weight, v_weight, out_weight, q_bias, k_bias, v_bias, out_bias,
-                  B, C, H, W, num_groups, num_heads, dtype, options, workspace, workspace_bytes,
-                  stream);
+  return ssa::run(-1, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight, out_weight,
+                  q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups, num_heads, dtype,
+                  options, workspace, workspace_bytes, stream);
 }
 
 ssa_status ssa_forward_stage(int stage, const void* x, void* out, const void* norm_weight,
@@ -239,10 +253,19 @@ ssa_status ssa_forward_stage(int stage, const void* x, void* out, const void* no
                              int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
                              int64_t num_heads, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  if (stage < SSA_STAGE_GN_STATS || stage > SSA_STAGE_OUT_PROJ) return SSA_E_STAGE;
-  return ssa::run(stage, stage, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight,
+  if (stage < SSA_STAGE_GN_STATS || stage > SSA_STAGE_QKV_ATTENTION) return SSA_E_STAGE;
+  return ssa::run(stage, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight,
                   out_weight, q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups,
                   num_heads, dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+int ssa_uses_fused_stage(int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
+                         int64_t num_heads, int dtype) {
+  ssa::Plan p;
+  bool empty = false;
+  if (ssa::make_plan(B, C, H, W, num_groups, num_heads, dtype, &p, &empty) != SSA_OK || empty)
+    return 0;
+  return ssa::fused_available(p) ? 1 : 0;
 }
 
 const char* ssa_status_string(int status) {
@@ -256,7 +279,8 @@ const char* ssa_status_string(int status) {
     case SSA_E_DTYPE: return "unknown dtype";
     case SSA_E_UNSUPPORTED:
       return "unsupported size: head size must be 1..128 (fp32) or 32/64/96/128 (bf16), even "
-             "with rotary embeddings, and 3*B*H*W*C below 2^31";
+             "with rotary embeddings, and 3*B*H*W*C below 2^31; the fused stage only where "
+             "ssa_uses_fused_stage() is 1";
     case SSA_E_WORKSPACE: return "workspace smaller than ssa_workspace_size()";
     case SSA_E_ALIAS: return "out or workspace overlaps another buffer";
     case SSA_E_ALIGN: return "a pointer is not 16-byte aligned";

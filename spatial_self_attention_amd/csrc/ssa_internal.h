@@ -70,6 +70,12 @@ hipError_t launch_qkv_proj(const Plan& p, const Args& a);
 hipError_t launch_attention(const Plan& p, const Args& a);
 hipError_t launch_out_proj(const Plan& p, const Args& a);
 
+// Q/K/V projections and attention in one kernel (SSA_STAGE_QKV_ATTENTION),
+// for the sizes fused_available() accepts: its O equals that of the QKV and
+// attention stages bit for bit.
+bool fused_available(const Plan& p);
+hipError_t launch_fused(const Plan& p, const Args& a);
+
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
 

@@ -168,8 +168,33 @@ def test_rejections(case, kw, want):
 
 
 def test_unknown_stage():
-    assert bnd.STATUS_NAMES[call("stage", stage=4, shape=OK_SHAPE)] == "SSA_E_STAGE"
+    assert bnd.STATUS_NAMES[call("stage", stage=5, shape=OK_SHAPE)] == "SSA_E_STAGE"
     assert bnd.STATUS_NAMES[call("stage", stage=-1, shape=OK_SHAPE)] == "SSA_E_STAGE"
+
+
+def test_fused_stage_outside_its_sizes_is_rejected():
+    # d = 32: the fused kernel does not cover it; the host says so, nothing launches
+    assert bnd.STATUS_NAMES[call("stage", stage=4, shape=OK_SHAPE)] == "SSA_E_UNSUPPORTED"
+
+
+# Without a GPU the library assumes 256 compute units (the MI355X count), so
+# the B * num_heads >= 256 rule reads the same here as on that device.
+@pytest.mark.parametrize("shape,want", [
+    ((64, 512, 14, 14, 32, 4, ssa.SSA_BF16), True),    # T = 196: 7 key blocks
+    ((64, 512, 16, 16, 32, 4, ssa.SSA_BF16), True),    # T = 256: 8 key blocks
+    ((22, 1536, 14, 14, 32, 12, ssa.SSA_BF16), True),  # the largest C the LDS table holds
+    ((64, 512, 12, 16, 32, 4, ssa.SSA_BF16), False),   # T = 192: 6 blocks, not instantiated
+    ((64, 512, 16, 17, 32, 4, ssa.SSA_BF16), False),   # T = 272 > 256
+    ((64, 512, 14, 15, 32, 4, ssa.SSA_BF16), False),   # T = 210, not a multiple of 4
+    ((63, 512, 14, 14, 32, 4, ssa.SSA_BF16), False),   # 252 (sample, head) pairs < 256 CUs
+    ((64, 512, 14, 14, 32, 8, ssa.SSA_BF16), False),   # d = 64
+    ((64, 512, 14, 14, 32, 4, ssa.SSA_F32), False),    # fp32
+    ((20, 1664, 14, 14, 32, 13, ssa.SSA_BF16), False),  # C past the coefficient table
+    ((64, 512, 14, 14, 7, 4, ssa.SSA_BF16), False),    # rejected arguments
+    ((0, 512, 14, 14, 32, 4, ssa.SSA_BF16), False),    # empty input
+])
+def test_uses_fused_stage(shape, want):
+    assert ssa.ssa_uses_fused_stage(*shape) is want
 
 
 @pytest.mark.parametrize("shape", [(0, 64, 8, 8, 8, 2, ssa.SSA_BF16),

@@ -31,8 +31,9 @@ def err(got, want, dtype):
     return e
 
 
-def run(wl: Workload, seed: int, stress=False, poison=True):
-    """Draw inputs, run the block on the GPU; return inputs, out and workspace."""
+def run(wl: Workload, seed: int, stress=False, poison=True, stages=None):
+    """Draw inputs, run the block on the GPU (or the listed stages in order);
+    return inputs, out and workspace."""
     x, p = draw(wl, seed, stress=stress)
     xg = x.to(DEV)
     pg = {k: v.to(DEV) for k, v in p.items()}
@@ -43,7 +44,11 @@ def run(wl: Workload, seed: int, stress=False, poison=True):
         ws.fill_(0xFF)          # NaN bit patterns in every float region
     print(f"[gpu] {wl.name} dtype={wl.dtype} B={wl.B} C={wl.C} H={wl.H} W={wl.W} "
           f"G={wl.num_groups} n={wl.num_heads} seed={seed} stress={stress}", flush=True)
-    ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws)
+    if stages is None:
+        ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws)
+    else:
+        for stage in stages:
+            ssa.forward_into(xg, pg, wl.num_groups, wl.num_heads, out, ws, stage=stage)
     torch.cuda.synchronize()
     return x, p, out, ws
 
@@ -76,7 +81,8 @@ STAGE_CASES = [
 
 @pytest.mark.parametrize("wl", STAGE_CASES, ids=lambda w: w.name)
 def test_stage_parity(wl):
-    x, p, out, ws = run(wl, 11)
+    # the four separate stages, so that Q, K and V are in the workspace
+    x, p, out, ws = run(wl, 11, stages=("gn_stats", "qkv", "attention", "out_proj"))
     st = ORA.forward_stages(*to_f64(x, p), wl.num_groups, wl.num_heads)
     B, C, T, n, d, G = wl.B, wl.C, wl.T, wl.num_heads, wl.d, wl.num_groups
     edt = wl.torch_dtype
