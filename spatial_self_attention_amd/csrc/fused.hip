@@ -52,24 +52,37 @@ struct FusedParams {
   float q_scale;        // log2(e) / sqrt(d)
 };
 
-constexpr int FGK = 32;        // input channels per step
-constexpr int FGP = FGK + 8;   // staging row pitch (bf16): 80-byte rows, conflict-free 16-byte reads
 constexpr int FNW = 8;         // waves per work-group
 constexpr int FNT = 64 * FNW;  // threads
+
+// Staging geometry of a pass that takes GK input channels per step.
+template <int GK>
+struct FGeom {
+  static constexpr int GP = GK + 8;      // row pitch (bf16): 16-byte reads of 8 rows hit distinct banks
+  static constexpr int CH = GK / 8;      // 16-byte chunks per weight row
+  static constexpr int RPV = FNT / CH;   // weight rows per round of one vector per thread
+  static constexpr int CQ = GK / 32;     // channel quads of x per thread
+  static constexpr int SUB = GK / 16;    // MFMA sub-steps per step
+};
 
 template <int D, int NB>
 struct FLayout {
   static constexpr int TOK = NB * 32;   // tokens, padded to whole 32-key blocks
   static constexpr int QP = D + 8;      // Q / K row pitch
   static constexpr int VP = TOK + 8;    // V^T row pitch
+  // pass 1 (Q): two staging buffers from 0; Q is written
+  // over them after the pass
+  static constexpr int QGK = 32, KVGK = 32;
+  static constexpr int QSZ = (D + TOK) * FGeom<QGK>::GP;
   static constexpr int QR = 0;          // Q (TOK x QP), passes 1-2
-  static constexpr int ST = TOK * QP;   // two staging buffers, passes 1-2
-  static constexpr int STW = 2 * D;     // staging: weight rows (K/V pass), then TOK token rows
-  static constexpr int STSZ = (STW + TOK) * FGP;
+  // pass 2 (K/V, 32 channels per step): two staging buffers after Q
+  static constexpr int ST = TOK * QP;
+  static constexpr int STSZ = (2 * D + TOK) * FGeom<KVGK>::GP;
   static constexpr int KR = 0;          // K (TOK x QP), step 3
   static constexpr int VR = TOK * QP;   // V^T (D x VP), step 3
-  static constexpr int A = ST + 2 * STSZ, B = VR + D * VP, C = FNW * 32 * QP;
-  static constexpr int ELEMS = A > B ? (A > C ? A : C) : (B > C ? B : C);
+  static constexpr int A = ST + 2 * STSZ, A1 = 2 * QSZ, B = VR + D * VP, C = FNW * 32 * QP;
+  static constexpr int AA = A > A1 ? A : A1;
+  static constexpr int ELEMS = AA > B ? (AA > C ? AA : C) : (B > C ? B : C);
   static_assert(ELEMS * 2 <= 160 * 1024, "the work-group's LDS fits one CU");
 };
 
@@ -82,47 +95,52 @@ constexpr int kFusedMaxC = 1536;  // fused_max_c<128, 8>() rounded down to whole
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // One step's loads in registers.  Thread (wave w, lane l): weight vectors
-// tid + FNT*i (row (v>>5)*8 + (v&7), channels 8*((v>>3)&3) ..), so that 8
+// v = tid + FNT*i, row ((v>>3) / CH)*8 + (v&7), chunk (v>>3) % CH, so that 8
 // consecutive lanes write one 16-byte column of 8 rows (distinct banks);
-// x: channels 4*(l&7) .. +3 of the step, tokens 4*((l>>3) + 8w) .. +3.
-// (The GroupNorm coefficients of the sample sit in an LDS table.)
-template <int NWV>
+// x: channels 4*(l&7) + 32q .. +3 (q < CQ) of the step, tokens
+// 4*((l>>3) + 8w) .. +3.  (The GroupNorm coefficients of the sample sit in an
+// LDS table.)
+template <int GK, int R>
 struct FStage {
+  static constexpr int NWV = R / FGeom<GK>::RPV;
   bf16x8 w[NWV];
-  u32x2 x[4];
+  u32x2 x[4 * FGeom<GK>::CQ];
 };
 
 // Per-thread load addressing of one pass (R weight rows: rows 0..D-1 from
 // w[first], D..2D-1 from w[first+1]) through buffer resources: the
 // per-thread byte offsets are fixed, each step only moves a scalar offset.
 // (A tensor holds fewer than 2^31 elements, so bf16 byte offsets fit 32 bits.)
-template <int NWV>
+template <int GK, int R>
 struct FLoad {
+  static constexpr int NWV = R / FGeom<GK>::RPV;
   __amdgpu_buffer_rsrc_t rw[NWV];  // the weight matrix of vector i
-  int vw[NWV];                     // byte offset of vector i's row and channels at channel 0
+  int vw[NWV];                     // byte offset of vector i's row and chunk at channel 0
   __amdgpu_buffer_rsrc_t rx;
   int vx;                          // byte offset of x[b][4*(l&7)][4*tq]
   int xrow;                        // bytes between channel rows of x (2T)
 };
 
-template <int D, int R>
-__device__ __forceinline__ void f_setup(FLoad<R / 128>& ld, const FusedParams& fp, int first,
-                                        int b, int head, int tid, int wave, int lane, int B) {
+template <int D, int GK, int R>
+__device__ __forceinline__ void f_setup(FLoad<GK, R>& ld, const FusedParams& fp, int first,
+                                        int b, int head, int tid, int wave, int lane) {
+  typedef FGeom<GK> G;
+  static_assert(D % G::RPV == 0, "a round of weight rows lies in one matrix");
   const unsigned C = unsigned(fp.C), T = unsigned(fp.T);
 #pragma unroll
-  for (int i = 0; i < R / 128; ++i) {
+  for (int i = 0; i < FLoad<GK, R>::NWV; ++i) {
     const int v = tid + FNT * i;
-    const int r = ((v >> 5) << 3) | (v & 7);
-    const int which = first + (128 * i) / D;  // rows 128i .. 128i+127 lie in one matrix (D >= 128)
+    const int r = ((v >> 3) / G::CH) * 8 + (v & 7);
+    const int which = first + (G::RPV * i) / D;
     const bf16* w = which == 0 ? fp.w[0] : which == 1 ? fp.w[1] : fp.w[2];
     ld.rw[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(w), 0, int(C * C * 2u),
                                                   kRsrcWord3);
-    ld.vw[i] = int(((unsigned(head * D + r % D)) * C + unsigned((v >> 3) & 3) * 8u) * 2u);
+    ld.vw[i] = int((unsigned(head * D + r % D) * C + unsigned((v >> 3) % G::CH) * 8u) * 2u);
   }
   const unsigned tq = unsigned(min((lane >> 3) + 8 * wave, int(T) / 4 - 1));  // padding tokens repeat the last quad
   const unsigned c4 = 4u * unsigned(lane & 7);
   ld.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(fp.x), 0,
-                                            int(unsigned(B) * C * T * 2u), kRsrcWord3);
+                                            int(unsigned(fp.B) * C * T * 2u), kRsrcWord3);
   ld.vx = int(((unsigned(b) * C + c4) * T + 4u * tq) * 2u);
   ld.xrow = int(T * 2u);
 }
@@ -130,68 +148,73 @@ __device__ __forceinline__ void f_setup(FLoad<R / 128>& ld, const FusedParams& f
 // Every wave issues the same loads (a wave past the last token block reads
 // the clamped quad and writes nothing), so the number of loads in flight is
 // the same on every path and each step waits only for the loads it stores.
-template <int NWV>
-__device__ __forceinline__ void f_load(FStage<NWV>& sg, const FLoad<NWV>& ld, int k0) {
+template <int GK, int R>
+__device__ __forceinline__ void f_load(FStage<GK, R>& sg, const FLoad<GK, R>& ld, int k0) {
 #pragma unroll
-  for (int i = 0; i < NWV; ++i)
+  for (int i = 0; i < FLoad<GK, R>::NWV; ++i)
     sg.w[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ld.rw[i], ld.vw[i],
                                                                                 k0 * 2, 0));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    sg.x[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                            ld.rx, ld.vx, int(unsigned(k0 + j) * unsigned(ld.xrow)), 0));
+  for (int q = 0; q < FGeom<GK>::CQ; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sg.x[4 * q + j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+          ld.rx, ld.vx, int(unsigned(k0 + 32 * q + j) * unsigned(ld.xrow)), 0));
 }
 
-// Half p (0, 1) of writing a register stage (channels k0 ..) to a staging
-// buffer: weight vectors (p = 0), and tokens 2p, 2p+1 of the thread's quad,
-// normalised (GN(x) = a x + s in fp32, one bf16 rounding; (a, s) from the
-// sample's coefficient table cft in LDS).
-template <int D, int NWV>
-__device__ __forceinline__ void f_store(bf16* buf, const FStage<NWV>& sg, const float2* cft,
+// Part p (one per MFMA sub-step) of writing a register stage (channels
+// k0 ..) to a staging buffer: the weight vectors i with i % SUB == p, and two
+// of the thread's (channel quad, token) items, normalised (GN(x) = a x + s in
+// fp32, one bf16 rounding; (a, s) from the sample's coefficient table cft).
+template <int GK, int R>
+__device__ __forceinline__ void f_store(bf16* buf, const FStage<GK, R>& sg, const float2* cft,
                                         int k0, int tid, int wave, int lane, bool zact, int p) {
-  if (p == 0) {
+  typedef FGeom<GK> G;
 #pragma unroll
-    for (int i = 0; i < NWV; ++i) {
-      const int v = tid + FNT * i;
-      const int r = ((v >> 5) << 3) | (v & 7);
-      *reinterpret_cast<bf16x8*>(&buf[r * FGP + ((v >> 3) & 3) * 8]) = sg.w[i];
-    }
+  for (int i = 0; i < FStage<GK, R>::NWV; ++i) {
+    if (i % G::SUB != p) continue;
+    const int v = tid + FNT * i;
+    const int r = ((v >> 3) / G::CH) * 8 + (v & 7);
+    *reinterpret_cast<bf16x8*>(&buf[r * G::GP + ((v >> 3) % G::CH) * 8]) = sg.w[i];
   }
   if (zact) {
-    bf16* Zs = buf + 2 * D * FGP;
-    const int tq = (lane >> 3) + 8 * wave, c4 = 4 * (lane & 7);
+    bf16* Zs = buf + R * G::GP;
+    const int tq = (lane >> 3) + 8 * wave;
+    const int q = p / 2;  // items 2p, 2p+1: channel quad (2p)/4, tokens (2p)%4 ..
+    const int c4 = 4 * (lane & 7) + 32 * q;
     const f32x4 cf[2] = {*reinterpret_cast<const f32x4*>(&cft[k0 + c4]),
                          *reinterpret_cast<const f32x4*>(&cft[k0 + c4 + 2])};
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
-      const int u = 2 * p + uu;
+      const int u = (2 * p + uu) % 4;
       bf16x4 z;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float a = cf[j >> 1][(j & 1) * 2], sh = cf[j >> 1][(j & 1) * 2 + 1];
-        const unsigned w2 = sg.x[j][u >> 1];
+        const unsigned w2 = sg.x[4 * q + j][u >> 1];
         const float xv = __uint_as_float((u & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
         z[j] = static_cast<bf16>(fmaf(a, xv, sh));
       }
-      *reinterpret_cast<bf16x4*>(&Zs[(4 * tq + u) * FGP + c4]) = z;
+      *reinterpret_cast<bf16x4*>(&Zs[(4 * tq + u) * G::GP + c4]) = z;
     }
   }
 }
 
 // Sub-step s (16 channels) of one step for one wave: weight rows wrow ..
 // wrow+63 (2 blocks) against token blocks tb0 .. tb0+NV-1.
-template <int D, int NV, bool TR>
+template <int GK, int R, int NV, bool TR>
 __device__ __forceinline__ void f_mfma(f32x16 (&acc)[2][NV], const bf16* buf, int wrow, int tb0,
                                        int half, int col, int s) {
-  const bf16* Zs = buf + 2 * D * FGP;
+  constexpr int GP = FGeom<GK>::GP;
+  const bf16* Zs = buf + R * GP;
   const int ko = s * 16 + half * 8;
   bf16x8 fa[2], fb[NV];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    fa[i] = *reinterpret_cast<const bf16x8*>(&buf[(wrow + i * 32 + col) * FGP + ko]);
+    fa[i] = *reinterpret_cast<const bf16x8*>(&buf[(wrow + i * 32 + col) * GP + ko]);
 #pragma unroll
   for (int j = 0; j < NV; ++j)
-    fb[j] = *reinterpret_cast<const bf16x8*>(&Zs[((tb0 + j) * 32 + col) * FGP + ko]);
+    fb[j] = *reinterpret_cast<const bf16x8*>(&Zs[((tb0 + j) * 32 + col) * GP + ko]);
 #pragma unroll
   for (int j = 0; j < NV; ++j)
 #pragma unroll
@@ -205,11 +228,10 @@ __device__ __forceinline__ void f_mfma(f32x16 (&acc)[2][NV], const bf16* buf, in
 // .. +63 and token blocks TB*(w / (R/64)) .. +NV-1 (NV = TB except in the last
 // wave group, which takes the blocks left below NB); TR: the wave's rows are
 // V rows (swapped orientation).  st0/st1: the staging buffers.
-template <int D, int NB, int R, int TB, int NV, bool TR, typename Epi>
+template <int D, int NB, int GK, int R, int TB, int NV, bool TR, typename Epi>
 __device__ __forceinline__ void f_pass(const FusedParams& fp, int first, bf16* st0, bf16* st1,
                                        const float2* cft, int b, int head, int tid, int wave,
                                        int lane, Epi& epi) {
-  constexpr int NWV = R / 128;
   constexpr int WR = R / 64;
   const int half = lane >> 5, col = lane & 31;
   const int wrow = (wave % WR) * 64;
@@ -222,25 +244,25 @@ __device__ __forceinline__ void f_pass(const FusedParams& fp, int first, bf16* s
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  FLoad<NWV> ld;
-  f_setup<D, R>(ld, fp, first, b, head, tid, wave, lane, fp.B);
-  const int nk = fp.C / FGK;  // even, >= 2
-  FStage<NWV> s0, s1;
+  FLoad<GK, R> ld;
+  f_setup<D, GK, R>(ld, fp, first, b, head, tid, wave, lane);
+  const int nk = fp.C / GK;  // even (C is a multiple of 128), >= 2
+  FStage<GK, R> s0, s1;
   f_load(s0, ld, 0);
-  f_store<D>(st0, s0, cft, 0, tid, wave, lane, zact, 0);
-  f_store<D>(st0, s0, cft, 0, tid, wave, lane, zact, 1);
-  f_load(s1, ld, FGK);
+#pragma unroll
+  for (int p = 0; p < FGeom<GK>::SUB; ++p) f_store<GK, R>(st0, s0, cft, 0, tid, wave, lane, zact, p);
+  f_load(s1, ld, GK);
   // step ks reads rd; nxt (step ks+1) is written to wr when `more`; fre takes
   // the loads of step ks+2 when `load`
-  auto step = [&](const bf16* rd, bf16* wr, const FStage<NWV>& nxt, FStage<NWV>& fre, int ks,
-                  bool more, bool load) {
+  auto step = [&](const bf16* rd, bf16* wr, const FStage<GK, R>& nxt, FStage<GK, R>& fre,
+                  int ks, bool more, bool load) {
     __syncthreads();  // rd is complete; wr is no longer read
-    if (load) f_load(fre, ld, (ks + 2) * FGK);
+    if (load) f_load(fre, ld, (ks + 2) * GK);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < FGK / 16; ++s) {
-      f_mfma<D, NV, TR>(acc, rd, wrow, tb0, half, col, s);
-      if (more) f_store<D>(wr, nxt, cft, (ks + 1) * FGK, tid, wave, lane, zact, s);
+    for (int s = 0; s < FGeom<GK>::SUB; ++s) {
+      f_mfma<GK, R, NV, TR>(acc, rd, wrow, tb0, half, col, s);
+      if (more) f_store<GK, R>(wr, nxt, cft, (ks + 1) * GK, tid, wave, lane, zact, s);
     }
   };
   // the register stages alternate at compile time (nk is even); steps
@@ -257,7 +279,7 @@ __device__ __forceinline__ void f_pass(const FusedParams& fp, int first, bf16* s
 // f_pass for this wave's group: WT = 8 / (R/64) groups of TB token blocks,
 // the last one holding NB - (WT-1) TB of them.  epi(acc, NV, TR) runs after
 // the pass with the accumulators of the wave's NV blocks.
-template <int D, int NB, int R, int TB, bool TR, typename Epi>
+template <int D, int NB, int GK, int R, int TB, bool TR, typename Epi>
 __device__ __forceinline__ void f_pass_wave(const FusedParams& fp, int first, bf16* st0,
                                             bf16* st1, const float2* cft, int b, int head,
                                             int tid, int wave, int lane, Epi& epi) {
@@ -265,12 +287,12 @@ __device__ __forceinline__ void f_pass_wave(const FusedParams& fp, int first, bf
   constexpr int NVL = NB - (WT - 1) * TB;
   static_assert(NVL >= 1 && NVL <= TB, "every wave group has token blocks");
   if constexpr (NVL == TB) {
-    f_pass<D, NB, R, TB, TB, TR>(fp, first, st0, st1, cft, b, head, tid, wave, lane, epi);
+    f_pass<D, NB, GK, R, TB, TB, TR>(fp, first, st0, st1, cft, b, head, tid, wave, lane, epi);
   } else {
     if (wave / (R / 64) == WT - 1)
-      f_pass<D, NB, R, TB, NVL, TR>(fp, first, st0, st1, cft, b, head, tid, wave, lane, epi);
+      f_pass<D, NB, GK, R, TB, NVL, TR>(fp, first, st0, st1, cft, b, head, tid, wave, lane, epi);
     else
-      f_pass<D, NB, R, TB, TB, TR>(fp, first, st0, st1, cft, b, head, tid, wave, lane, epi);
+      f_pass<D, NB, GK, R, TB, TB, TR>(fp, first, st0, st1, cft, b, head, tid, wave, lane, epi);
   }
 }
 
@@ -287,7 +309,7 @@ __global__ __launch_bounds__(FNT, 1) void fused_bf16_kernel(FusedParams fp) {
   const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   const int b = lid / fp.n, head = lid - b * fp.n;
   const int T = fp.T, C = fp.C;
-  bf16* st0 = lds + L::ST;
+  bf16* st0 = lds + L::ST;  // K/V pass staging
   bf16* st1 = lds + L::ST + L::STSZ;
   for (int c = tid; c < C; c += FNT) cft[c] = fp.coef[int64_t(b) * C + c];
   __syncthreads();  // the table is read from the first staging writes on
@@ -300,6 +322,7 @@ __global__ __launch_bounds__(FNT, 1) void fused_bf16_kernel(FusedParams fp) {
       constexpr int NV = decltype(nv)::value;
       int half = lane >> 5, col = lane & 31;
       asm volatile("" : "+v"(half), "+v"(col));  // keep the epilogue's addressing below the loop
+      __syncthreads();  // every wave is done with the staging buffers Q is written over
       const bf16* bq = fp.bias[0];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -318,7 +341,8 @@ __global__ __launch_bounds__(FNT, 1) void fused_bf16_kernel(FusedParams fp) {
           }
         }
     };
-    f_pass_wave<D, NB, D, TB, false>(fp, 0, st0, st1, cft, b, head, tid, wave, lane, epi);
+    f_pass_wave<D, NB, L::QGK, D, TB, false>(fp, 0, lds, lds + L::QSZ, cft, b, head, tid, wave,
+                                              lane, epi);
   }
 
   // ---- 2. K/V pass: rows 0..D-1 = K channels, D..2D-1 = V channels ----
@@ -378,9 +402,11 @@ __global__ __launch_bounds__(FNT, 1) void fused_bf16_kernel(FusedParams fp) {
       }
     };
     if (wrow >= D)  // wave-uniform: V rows take the swapped orientation
-      f_pass_wave<D, NB, 2 * D, TB, true>(fp, 1, st0, st1, cft, b, head, tid, wave, lane, epi);
+      f_pass_wave<D, NB, L::KVGK, 2 * D, TB, true>(fp, 1, st0, st1, cft, b, head, tid, wave, lane,
+                                                  epi);
     else
-      f_pass_wave<D, NB, 2 * D, TB, false>(fp, 1, st0, st1, cft, b, head, tid, wave, lane, epi);
+      f_pass_wave<D, NB, L::KVGK, 2 * D, TB, false>(fp, 1, st0, st1, cft, b, head, tid, wave, lane,
+                                                   epi);
   }
   __syncthreads();  // K and V^T are complete
 
