@@ -411,6 +411,149 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel with two 32-query blocks per wave
+// ---------------------------------------------------------------------------
+// Every K and V^T operand fragment a wave reads from LDS feeds two MFMAs, one
+// per query block, so the LDS reads per MFMA are half those of the one-block
+// kernel.  Per 32-key sub-block: the K fragments (read one sub-block ahead),
+// the scores of both blocks, then block by block the softmax and O^T += V^T P^T,
+// so one block's softmax runs beside the other block's MFMAs.
+
+// Online softmax of one query block's 32-key sub-block (scores relative to
+// its running max): the bf16 probabilities in MFMA B-operand order and the
+// row-sum update; m is raised (and O, l rescaled) as in softmax_block.
+template <int D, int QB, bool MASK>
+__device__ __forceinline__ void softmax_qb(AttnState<D, QB>& st, int qb, f32x16& s,
+                                           bf16x8 (&pb)[2], int kfirst, int T, int half,
+                                           bool first) {
+  if constexpr (MASK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kfirst + 8 * (r >> 2) + 4 * half + (r & 3) >= T) s[r] = -INFINITY;
+  }
+  float part = probs(pb, s, 0.f);
+  if (first || __builtin_amdgcn_ballot_w64(!(part <= kLazySum))) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = halves_max(mx);
+    const float m_new = first ? mx : fmaxf(st.m[qb], st.m[qb] + mx);
+    const float delta = m_new - st.m[qb];
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      st.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[qb][db][r] *= alpha;
+    }
+    st.m[qb] = m_new;
+    // in place, so that the common path (no raise) needs no copy of nm
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.nm[qb][r] = first ? -m_new : st.nm[qb][r] - delta;
+    part = probs(pb, s, delta);
+  }
+  st.l[qb] += part;
+}
+
+// O^T += V^T P^T of one query block.
+template <int D, int QB>
+__device__ __forceinline__ void pv_qb(AttnState<D, QB>& st, int qb, const bf16x8 (&pb)[2],
+                                      const VFrag<D>& f) {
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[gp][db], pb[gp], st.o[qb][db], 0, 0, 0);
+}
+
+// One key tile for one wave holding two query blocks.  kf holds the K
+// fragments of the tile's first sub-block on entry (each sub-block reads the
+// next one's while its scores are formed).
+template <int D, int KT, bool MASK>
+__device__ __forceinline__ void attend_tile2(AttnState<D, 2>& st, KFrag<D>& kf, const bf16* buf,
+                                             int k0, int T, int half, int col, bool first) {
+  typedef Tile<D, 2, KT> TL;
+  constexpr int NKB = TL::NKB;
+  const bf16* Vs = buf + TL::KSZ;
+  const int nv = MASK ? min(NKB, (T - k0 + 31) / 32) : NKB;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    if (MASK && kb >= nv) break;
+    f32x16 s[2];
+    qk_mfma<D, 2>(s, st, kf);
+    VFrag<D> vf;
+    read_v<D, 2, KT>(vf, Vs, kb, half, col);
+    if (kb + 1 < nv) read_k<D, 2, KT>(kf, buf, kb + 1, half, col);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      bf16x8 pb[2];
+      softmax_qb<D, 2, MASK>(st, qb, s[qb], pb, k0 + kb * 32, T, half, first && kb == 0);
+      pv_qb<D, 2>(st, qb, pb, vf);
+    }
+  }
+}
+
+// NW waves x 64 queries per work-group.
+template <int D, int KT, int NW, int MINB>
+__global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap) {
+  typedef Tile<D, 2, KT, NW> TL;
+  constexpr int kStage = NW * 64 * (D + 8);  // output staging, after the key tiles
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * TL::BUF > kStage ? 2 * TL::BUF : kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
+  const int qtile = lid % ap.qtiles;
+  const int bh = lid / ap.qtiles;  // b * n + head
+  const int head = bh % ap.n, b = bh / ap.n;
+  const int T = ap.T;
+
+  const bf16* Q = static_cast<const bf16*>(ap.q) + int64_t(bh) * T * D;
+  const bf16* K = static_cast<const bf16*>(ap.k) + int64_t(bh) * T * D;
+  const bf16* Vt = static_cast<const bf16*>(ap.vt) + int64_t(bh) * D * ap.Tp;
+
+  AttnState<D, 2> st;
+  init_state<D, 2>(st, Q, qtile * TL::QT + wave * TL::QPW, T, half, col);
+
+  const int ntiles = (T + KT - 1) / KT;
+  const int nfull = T / KT;
+  Prefetch<D, 2, KT, NW> pf;
+  if (nfull > 0)
+    load_tile<D, 2, KT, NW, false>(pf, K, Vt, ap.Tp, 0, T, tid);
+  else
+    load_tile<D, 2, KT, NW, true>(pf, K, Vt, ap.Tp, 0, T, tid);
+  store_tile<D, 2, KT, NW>(lds, pf, tid);
+
+  KFrag<D> kf;
+  __syncthreads();
+  read_k<D, 2, KT>(kf, lds, 0, half, col);
+  for (int j = 0; j < nfull; ++j) {
+    const int kn = (j + 1) * KT;
+    if (j + 1 < nfull)
+      load_tile<D, 2, KT, NW, false>(pf, K, Vt, ap.Tp, kn, T, tid);
+    else if (j + 1 < ntiles)
+      load_tile<D, 2, KT, NW, true>(pf, K, Vt, ap.Tp, kn, T, tid);
+    bf16* cur = lds + (j & 1) * TL::BUF;
+    bf16* nxt = lds + ((j + 1) & 1) * TL::BUF;
+    attend_tile2<D, KT, false>(st, kf, cur, j * KT, T, half, col, j == 0);
+    // the other buffer held tile j-1, which every wave finished before the
+    // barrier that ended the previous iteration
+    if (j + 1 < ntiles) store_tile<D, 2, KT, NW>(nxt, pf, tid);
+    __syncthreads();  // tile j+1 is in place; tile j is free
+    if (j + 1 < ntiles) read_k<D, 2, KT>(kf, nxt, 0, half, col);
+  }
+  if (nfull < ntiles)  // the partial last tile
+    attend_tile2<D, KT, true>(st, kf, lds + (nfull & 1) * TL::BUF, nfull * KT, T, half, col,
+                              nfull == 0);
+
+  __syncthreads();  // every wave is done with the key tiles: LDS becomes staging
+  write_o<D, 2>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col, lane,
+                lds + wave * 64 * (D + 8));
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel
 // ---------------------------------------------------------------------------
 constexpr int FQT = 64, FKT = 32;
@@ -508,6 +651,14 @@ void launch_bf16_v(AttnParams ap, int64_t bh, hipStream_t stream) {
   attn_bf16_kernel<D, QB, KT, NW, REL><<<dim3(unsigned(bh * ap.qtiles)), TL::NTHR, 0, stream>>>(ap);
 }
 
+template <int D, int KT, int NW, int MINB>
+void launch_bf16_2(AttnParams ap, int64_t bh, hipStream_t stream) {
+  typedef Tile<D, 2, KT, NW> TL;
+  ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
+  attn2_bf16_kernel<D, KT, NW, MINB><<<dim3(unsigned(bh * ap.qtiles)), TL::NTHR, 0, stream>>>(ap);
+}
+
+
 // The relative-position variant comes in the 4-wave shape only.  Its table
 // slices go through LDS when every (query tile, key tile) pair's slice fits
 // kRelSlice entries: a query tile spans at most ceil((QT-1)/W) + 1 grid rows
@@ -525,6 +676,29 @@ void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
   } else {
     launch_bf16_v<D, QB, KT, NW, 0>(ap, bh, stream);
   }
+}
+
+// d = 64 without the relative-position bias, long sequences: the two-block
+// kernel reads half the LDS operand bytes per MFMA but holds twice the
+// queries per wave, so it needs whole rounds of work-groups to pay.  512-query
+// work-groups (8 waves, key tiles of 128, one per CU) when the query tiles
+// fill whole rounds of the CUs or many of them; 256-query work-groups (4
+// waves, key tiles of 64, two per CU) when they fill at least one round;
+// otherwise (shorter or fewer sequences) the one-block kernel, whose
+// 128-query work-groups spread the work more evenly.
+void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream) {
+  if (ap.rel == nullptr && p.T >= 1024) {
+    const int64_t t512 = bh * ((p.T + 511) / 512), t256 = bh * ((p.T + 255) / 256);
+    if (t512 % p.cus == 0 || t512 >= 4 * int64_t(p.cus)) {
+      launch_bf16_2<64, 128, 8, 1>(ap, bh, stream);
+      return;
+    }
+    if (t256 >= 2 * int64_t(p.cus)) {
+      launch_bf16_2<64, 64, 4, 2>(ap, bh, stream);
+      return;
+    }
+  }
+  launch_bf16<64, 1, 64, 4>(ap, bh, stream);
 }
 
 }  // namespace
@@ -554,7 +728,7 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
       case 32: launch_bf16<32, 1, 64, 4>(ap, bh, a.stream); break;
       case 64:
         if (wide) launch_bf16<64, 1, 64, 8>(ap, bh, a.stream);
-        else launch_bf16<64, 1, 64, 4>(ap, bh, a.stream);
+        else launch_bf16_64(p, ap, bh, a.stream);
         break;
       case 96: launch_bf16<96, 1, 64, 4>(ap, bh, a.stream); break;
       default:

@@ -159,3 +159,28 @@ def options_f64(opts: dict) -> dict:
     f = lambda t: None if t is None else t.to(torch.float64).numpy()
     return {"rel_pos_table": f(opts["rel_pos_table"]), "q_norm_gamma": f(opts["q_norm_gamma"]),
             "k_norm_gamma": f(opts["k_norm_gamma"]), "rope_on": bool(opts["rope"])}
+
+
+def draw_qkv(B: int, n: int, T: int, d: int, seed: int, kind: str = "peaked"):
+    """Seeded per-head query, key and value tensors (B, n, T, d), bf16, for
+    tests of the attention stage alone (written straight into the workspace).
+
+    The query tensor is the one the attention stage reads: scores are
+    2^(q . k), i.e. q already carries the score scale.
+    * "peaked": q, k ~ N(0, 0.9) (score std near 6 in log2 units), v ~ N(0, 1);
+    * "ramp": q ~ N(1, 0.2) and k ~ N(0, 0.2) + 4 t / T for key t, so scores
+      grow along the key axis (the running maximum rises in every key block
+      and early keys' weights underflow), v ~ N(0, 1).
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "peaked":
+        q = 0.9 * rng.standard_normal((B, n, T, d))
+        k = 0.9 * rng.standard_normal((B, n, T, d))
+    elif kind == "ramp":
+        q = 1.0 + 0.2 * rng.standard_normal((B, n, T, d))
+        k = 0.2 * rng.standard_normal((B, n, T, d)) + (4.0 * np.arange(T) / T)[None, None, :, None]
+    else:
+        raise ValueError(kind)
+    v = rng.standard_normal((B, n, T, d))
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).contiguous()
+    return to(q), to(k), to(v)
