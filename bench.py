@@ -1,14 +1,19 @@
 """Throughput of the spatial self-attention block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I] [--no-cpu]
-                    [--options relpos,qknorm,rope]
+                    [--eager] [--options relpos,qknorm,rope]
 
 A step is one ssa_forward over one batch of the selected workload (GroupNorm
 statistics, QKV projection, flash attention, output projection + residual;
 where the library fuses them, projection and attention are one kernel), with
-inputs already resident in HBM.  W untimed steps, then exactly K steps
+inputs already resident in HBM.  W untimed steps (and more untimed steps for
+--settle seconds, so the GPU's clocks have ramped up), then exactly K steps
 between two device synchronisations; the value is block TFLOP/s
-(8BTC^2 + 4BT^2C flops per step).  Prints one JSON line.
+(8BTC^2 + 4BT^2C flops per step).  The K steps are captured once into a HIP
+graph and replayed (every kernel of every step runs; only the host launch
+gaps between them go), as a deployment would run the block; the rate of K
+eager ssa_forward calls is reported beside it (`other_launch`), and --eager
+makes that one the value.  Prints one JSON line.
 
 Also reported:
 * per-kernel average durations from HIP events on the launch stream, each
@@ -43,11 +48,24 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_CONFIG = 1          # BoTNet-c5: B64 C512 14x14 G32 n4 (d=128), bf16
 
 
-def source_digest() -> str:
-    """Hash of the kernel sources, to tell whether stored counters still apply."""
+# The sources each stage's kernels are built from (its .hip file and the
+# headers it includes): stored counters stay valid while these are unchanged.
+STAGE_SOURCES = {
+    "gn_stats": ("gn_stats.hip", "ssa_internal.h"),
+    "qkv": ("projections.hip", "qk_post.hip", "ssa_internal.h"),
+    "attention": ("attention.hip", "attn_core.h", "ssa_internal.h"),
+    "qkv_attention": ("fused.hip", "attn_core.h", "ssa_internal.h"),
+    "out_proj": ("projections.hip", "ssa_internal.h"),
+}
+
+
+def source_digest(stage: str = None) -> str:
+    """Hash of the kernel sources (all, or those of one stage's kernels), to
+    tell whether stored counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "spatial_self_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = sorted(os.listdir(csrc)) if stage is None else sorted(STAGE_SOURCES[stage])
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -71,7 +89,7 @@ def stage_work(wl):
 STAGE_KERNELS = {
     "gn_stats": "gn_stats_kernel (+ gn_finalize_kernel when segments are split)",
     "qkv": "gemm_bf16_kernel<0>",
-    "attention": "attn_bf16_kernel",
+    "attention": "attn_bf16_kernel / attn2_bf16_kernel",
     "qkv_attention": "fused_bf16_kernel",
     "out_proj": "gemm_bf16_kernel<1>",
 }
@@ -86,10 +104,10 @@ def stored_traffic(stage: str, wl_name: str):
         data = json.load(open(path))
     except ValueError:
         return None
-    if data.get("source_digest") != source_digest():
-        return None
     ent = data.get("entries", {}).get(f"{wl_name}|{stage}")
-    return None if ent is None else ent.get("bytes_per_launch")
+    if ent is None or ent.get("source_digest") != source_digest(stage):
+        return None
+    return ent.get("bytes_per_launch")
 
 
 def cpu_baseline(wl, seed, budget_s=12.0):
@@ -123,14 +141,17 @@ def cpu_baseline(wl, seed, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed steps for this long after the warm-up steps (clock ramp)")
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--options", default="",
                     help="comma list of optional steps to switch on: relpos, qknorm, rope")
-    ap.add_argument("--graph", action="store_true",
-                    help="time K steps replayed from one HIP graph instead of eager launches")
+    ap.add_argument("--eager", action="store_true",
+                    help="time K eager launches of the step instead of K steps replayed from "
+                         "one HIP graph (both are measured; this picks which one is `value`)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 10 device-to-device copies of BYTES each (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to HBM bytes)")
@@ -181,31 +202,49 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # then keep stepping (untimed) for --settle seconds: a few warm-up steps of
+    # a short workload end before the GPU's clocks have ramped up
+    t_end = time.perf_counter() + args.settle
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
 
-    if args.graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    def timed(graph: bool) -> float:
+        """Seconds for exactly K steps between two device synchronisations."""
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(args.steps):
+                    step()
+            torch.cuda.synchronize()
+            g.replay()  # untimed: the first replay uploads the graph
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        if graph:
+            g.replay()
+        else:
             for _ in range(args.steps):
                 step()
+        e1.record(stream)
         torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    if args.graph:
-        g.replay()
-    else:
-        for _ in range(args.steps):
-            step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_s = e0.elapsed_time(e1) / 1e3
-    elapsed = max(wall, gpu_s)
+        wall = time.perf_counter() - t0
+        return max(wall, e0.elapsed_time(e1) / 1e3)
+
+    # The step as a deployment runs it: captured once into a HIP graph (all of
+    # its kernels, every step), so host launch gaps do not sit between them;
+    # the eager rate (one ssa_forward call per step) is reported beside it.
+    el = {"graph": timed(True), "eager": timed(False)}
+    launch = "eager" if args.eager else "graph"
+    elapsed = el[launch]
     ms_per_step = elapsed / args.steps * 1e3
     tflops = wl.flops() * args.steps / elapsed / 1e12
+    other = "graph" if launch == "eager" else "eager"
+    alt = {"launch": other, "value": round(wl.flops() * args.steps / el[other] / 1e12, 3),
+           "ms_per_step": round(el[other] / args.steps * 1e3, 5)}
 
     if opts is not None:
         print(json.dumps({
@@ -215,8 +254,8 @@ def main():
             "data": "synthetic (seeded, workload distributions)",
             "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
                        "num_groups": wl.num_groups, "num_heads": wl.num_heads, "d": wl.d,
-                       "launch": "graph" if args.graph else "eager", "options": names},
-            "kernels": None, "roofline": None, "cpu_baseline": None,
+                       "launch": launch, "options": names},
+            "other_launch": alt, "kernels": None, "roofline": None, "cpu_baseline": None,
             "source_digest": source_digest()}), flush=True)
         return
 
@@ -274,7 +313,8 @@ def main():
         "data": "synthetic (seeded, workload distributions)",
         "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W,
                    "num_groups": wl.num_groups, "num_heads": wl.num_heads, "d": wl.d,
-                   "launch": "graph" if args.graph else "eager"},
+                   "launch": launch},
+        "other_launch": alt,
         "pixels_per_s": round(wl.B * wl.T / elapsed * args.steps, 1),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "gn_stats_GBps": round(gn_bytes / per_stage["gn_stats"] / 1e9, 1),

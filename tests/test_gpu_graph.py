@@ -1,7 +1,7 @@
 """The block replayed from a captured HIP graph.
 
 Callers capture ssa_forward / ssa_forward_ex into graphs (bench.py times the
-stages that way).  A graph is captured once, then replayed several times with
+step and its stages that way).  A graph is captured once, then replayed several times with
 the inputs changed in place between replays and an eager call (own output and
 workspace) and a synchronisation in between; every replay must equal the eager
 result bit for bit (the same kernels on the same inputs).
@@ -22,10 +22,13 @@ CASES = [
     (Workload("bf16 d64 12x13", "bf16", 2, 128, 12, 13, 8, 2),
      dict(rel_pos=True, qk_norm=True, rope=True)),                    # every optional step
     (WORKLOADS[0], {}),                                               # fp32
+    (WORKLOADS[3], {}),                     # LDM level-1: d64, long sequences, one-block kernel
+    (WORKLOADS[4], {}),                     # high-res: the two-block attention kernel
 ]
 
 
-@pytest.mark.parametrize("wl,flags", CASES, ids=["bf16-d64", "bf16-d128-8wave", "bf16-options", "fp32"])
+@pytest.mark.parametrize("wl,flags", CASES, ids=["bf16-d64", "bf16-d128-8wave", "bf16-options", "fp32",
+                                                 "bf16-ldm-level1", "bf16-high-res"])
 def test_graph_replays_equal_eager(wl, flags):
     x, p = draw(wl, 61)
     xg = x.to(DEV)
