@@ -110,11 +110,14 @@ def test_relpos_wide_image(stress):
     assert e <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("idx", [1, 3])
-def test_options_full_size_sampled(idx):
+# Every option on (the relative-position bias keeps the one-block attention
+# kernel), and query/key normalisation with rotary embeddings at the
+# high-resolution workload, where the two-query-block attention kernel runs.
+@pytest.mark.parametrize("idx,rel", [(1, True), (3, True), (4, False)], ids=["1-all", "3-all", "4-qknorm-rope"])
+def test_options_full_size_sampled(idx, rel):
     wl = WORKLOADS[idx]
     x, p, opts, out = run_case(wl, 1000 + idx, False, drop_bias=("k_bias",),
-                               rel_pos=True, rope=True, qk_norm=True)
+                               rel_pos=rel, rope=True, qk_norm=True)
     x64, p64 = to_f64(x, p)
     og = out.double().cpu().numpy().reshape(wl.B, wl.C, wl.T)
     assert np.isfinite(og).all()
