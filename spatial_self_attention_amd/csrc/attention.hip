@@ -128,6 +128,41 @@ __device__ __forceinline__ void store_tile(bf16* buf, const Prefetch<D, QB, KT, 
   }
 }
 
+// Global -> LDS for one full K and V^T tile without VGPRs: buffer loads that
+// write LDS directly, 16 bytes per lane, each wave instruction filling 64
+// consecutive 16-byte chunks of the tile buffer (a K row is D/8 chunks and one
+// chunk of padding, a V^T row KT/8 and one: the padding chunks load the row's
+// first chunk again and are never read).  The rows' padding keeps the operand
+// fragment reads free of bank conflicts, as with the register path.
+template <int D, int QB, int KT, int NW>
+__device__ __forceinline__ void dma_tile(bf16* buf, const bf16* K, const bf16* Vt, int Tp, int k0,
+                                         int T, int wave, int lane) {
+  typedef Tile<D, QB, KT, NW> TL;
+  constexpr int KC = TL::KP / 8, VC = TL::VP / 8;  // 16-byte chunks per row
+  constexpr int NK = KT * KC, NV = D * VC;         // chunks per region
+  static_assert(NK % 64 == 0 && NV % 64 == 0, "every wave instruction stays in one region");
+  constexpr int NI = (NK + NV) / 64;               // wave instructions per tile
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + int64_t(k0) * D, int64_t(T - k0) * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vt + k0, (int64_t(D) * Tp - k0) * 2);
+#pragma unroll
+  for (int i0 = 0; i0 < NI; i0 += NW) {
+    const int i = i0 + wave;  // wave-uniform
+    if (i < NI) {
+      bf16* dst = buf + i * 64 * 8;  // this instruction's chunks (the LDS base goes to M0)
+      const int c = i * 64 + lane;
+      if (i * 64 < NK) {
+        const int r = c / KC, ch = c % KC;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, dst, 16, (r * D + (ch < D / 8 ? ch : 0) * 8) * 2,
+                                                 0, 0, 0);
+      } else {
+        const int r = (c - NK) / VC, ch = (c - NK) % VC;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, dst, 16,
+                                                 (r * Tp + (ch < KT / 8 ? ch : 0) * 8) * 2, 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <int D, int QB, int KT>
 __device__ __forceinline__ void read_k(KFrag<D>& f, const bf16* Ks, int kb, int half, int col) {
   typedef Tile<D, QB, KT> TL;
@@ -584,12 +619,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
 
   const int ntiles = (T + KT - 1) / KT;
   const int nfull = T / KT;
-  Prefetch<D, 2, KT, NW> pf;
-  if (nfull > 0)
-    load_tile<D, 2, KT, NW, false>(pf, K, Vt, ap.Tp, 0, T, tid);
-  else
-    load_tile<D, 2, KT, NW, true>(pf, K, Vt, ap.Tp, 0, T, tid);
-  store_tile<D, 2, KT, NW>(lds, pf, tid);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // Full tiles go global -> LDS directly (no prefetch registers): tile j+1's
+  // loads are issued into the free buffer before tile j is used, and the
+  // barrier that ends tile j waits for them.  The partial last tile (keys past
+  // T zeroed) goes through registers once, after the full tiles.
+  if (nfull > 0) dma_tile<D, 2, KT, NW>(lds, K, Vt, ap.Tp, 0, T, wv, lane);
 
   Pipe<D> pp;
   {
@@ -601,28 +636,33 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
       for (int db = 0; db < D / 32; ++db) pp.vf.a[gp][db] = z;
   }
   __syncthreads();
-  read_k<D, 2, KT>(pp.kf, lds, 0, half, col);
-  if (nfull > 0) qk_qb<D>(pp.s0, st, 0, pp.kf);
+  if (nfull > 0) {
+    read_k<D, 2, KT>(pp.kf, lds, 0, half, col);
+    qk_qb<D>(pp.s0, st, 0, pp.kf);
+  }
   for (int j = 0; j < nfull; ++j) {
-    const int kn = (j + 1) * KT;
-    if (j + 1 < nfull)
-      load_tile<D, 2, KT, NW, false>(pf, K, Vt, ap.Tp, kn, T, tid);
-    else if (j + 1 < ntiles)
-      load_tile<D, 2, KT, NW, true>(pf, K, Vt, ap.Tp, kn, T, tid);
     bf16* cur = lds + (j & 1) * TL::BUF;
     bf16* nxt = lds + ((j + 1) & 1) * TL::BUF;
-    pipe_tile<D, KT>(st, pp, cur, j * KT, T, half, col, j == 0);
     // the other buffer held tile j-1, which every wave finished before the
     // barrier that ended the previous iteration
-    if (j + 1 < ntiles) store_tile<D, 2, KT, NW>(nxt, pf, tid);
+    if (j + 1 < nfull) dma_tile<D, 2, KT, NW>(nxt, K, Vt, ap.Tp, (j + 1) * KT, T, wv, lane);
+    pipe_tile<D, KT>(st, pp, cur, j * KT, T, half, col, j == 0);
     __syncthreads();  // tile j+1 is in place; tile j is free
-    if (j + 1 < ntiles) read_k<D, 2, KT>(pp.kf, nxt, 0, half, col);
-    if (j + 1 < nfull) qk_qb<D>(pp.s0, st, 0, pp.kf);
+    if (j + 1 < nfull) {
+      read_k<D, 2, KT>(pp.kf, nxt, 0, half, col);
+      qk_qb<D>(pp.s0, st, 0, pp.kf);
+    }
   }
   pv_qb<D, 2>(st, 1, pp.pb1, pp.vf);
-  if (nfull < ntiles)  // the partial last tile
-    attend_tile2<D, KT, true, NW == 8>(st, pp.kf, lds + (nfull & 1) * TL::BUF, nfull * KT, T, half,
-                                       col, nfull == 0);
+  if (nfull < ntiles) {  // the partial last tile
+    bf16* buf = lds + (nfull & 1) * TL::BUF;
+    Prefetch<D, 2, KT, NW> pf;
+    load_tile<D, 2, KT, NW, true>(pf, K, Vt, ap.Tp, nfull * KT, T, tid);
+    store_tile<D, 2, KT, NW>(buf, pf, tid);
+    __syncthreads();
+    read_k<D, 2, KT>(pp.kf, buf, 0, half, col);
+    attend_tile2<D, KT, true, NW == 8>(st, pp.kf, buf, nfull * KT, T, half, col, nfull == 0);
+  }
 
   __syncthreads();  // every wave is done with the key tiles: LDS becomes staging
   write_o<D, 2>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col, lane,
