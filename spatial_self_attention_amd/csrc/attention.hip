@@ -450,9 +450,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<
 // ---------------------------------------------------------------------------
 // Every K and V^T operand fragment a wave reads from LDS feeds two MFMAs, one
 // per query block, so the LDS reads per MFMA are half those of the one-block
-// kernel.  Per 32-key sub-block: the K fragments (read one sub-block ahead),
-// the scores of both blocks, then block by block the softmax and O^T += V^T P^T,
-// so one block's softmax runs beside the other block's MFMAs.
+// kernel (at the price of 256 VGPRs: two waves per SIMD).  Full key tiles come
+// from global memory straight into LDS (dma_tile) and are walked by pipe_tile,
+// which issues each block's softmax beside eight MFMAs that do not wait for
+// it; the partial last tile goes through registers and attend_tile2 (both
+// blocks' scores, then block by block the softmax and O^T += V^T P^T).
 
 // Online softmax of one query block's 32-key sub-block (scores relative to
 // its running max): the bf16 probabilities in MFMA B-operand order and the
