@@ -49,6 +49,7 @@ struct AttnParams {
   void* o;         // (B, T, C)
   int T, Tp, n, d, C;
   int qtiles;      // query tiles per (b, head)
+  int tile0;       // two-block kernels: first (b, head, query tile) of this launch
   float scale;     // log2(e) / sqrt(d) (fp32 path; log2(e) with query/key normalisation)
   const void* rel; // ((2H-1)(2W-1), n) relative-position table, or NULL
   int H, W;
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
+  const int lid = ap.tile0 + xcd_remap(int(blockIdx.x), int(gridDim.x));
   const int qtile = lid % ap.qtiles;
   const int bh = lid / ap.qtiles;  // b * n + head
   const int head = bh % ap.n, b = bh / ap.n;
@@ -669,6 +670,104 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
   __syncthreads();  // every wave is done with the key tiles: LDS becomes staging
   write_o<D, 2>(st, ap, b, head, qtile * TL::QT + wave * TL::QPW, half, col, lane,
                 lds + wave * 64 * (D + 8));
+}
+
+// The 256-query tiles of a partial last round: 8 waves, the two halves of the
+// work-group (waves 0-3 and 4-7) taking the same 256 queries against the two
+// halves of the key tiles, each half with its own tile stream, so a CU that
+// would run one 4-wave work-group alone keeps two waves per SIMD.  Half 1
+// leaves (O, m, l) in LDS and half 0 merges:
+//   O = O_0 2^(m_0 - M) + O_1 2^(m_1 - M),  l likewise,  M = max(m_0, m_1).
+// Needs an even number of key tiles, all full.
+template <int D, int KT>
+__global__ __launch_bounds__(512, 1) void attn2s_bf16_kernel(AttnParams ap) {
+  typedef Tile<D, 2, KT, 4> TL;  // one half's geometry
+  constexpr int kState = 4 * 64 * (2 * (D / 32) * 16 + 4);  // floats: half 1's O, m, l
+  constexpr int kMerge = kState * 2 + 4 * 64 * (D + 8);     // + half 0's output staging (bf16)
+  // 2 halves x 2 tile buffers; after the tiles, the merge
+  __shared__ __attribute__((aligned(16))) bf16 lds[4 * TL::BUF > kMerge ? 4 * TL::BUF : kMerge];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int hk = __builtin_amdgcn_readfirstlane(wave >> 2);  // key half
+  const int gw = __builtin_amdgcn_readfirstlane(wave & 3);   // wave within the half
+  const int lid = ap.tile0 + xcd_remap(int(blockIdx.x), int(gridDim.x));
+  const int qtile = lid % ap.qtiles;
+  const int bh = lid / ap.qtiles;
+  const int head = bh % ap.n, b = bh / ap.n;
+  const int T = ap.T;
+  const bf16* Q = static_cast<const bf16*>(ap.q) + int64_t(bh) * T * D;
+  const bf16* K = static_cast<const bf16*>(ap.k) + int64_t(bh) * T * D;
+  const bf16* Vt = static_cast<const bf16*>(ap.vt) + int64_t(bh) * D * ap.Tp;
+  const int qbase = qtile * TL::QT + gw * TL::QPW;
+
+  AttnState<D, 2> st;
+  init_state<D, 2>(st, Q, qbase, T, half, col);
+  const int nh = T / KT / 2;  // key tiles per half
+  const int t0 = hk * nh;
+  bf16* mine = lds + hk * 2 * TL::BUF;
+  dma_tile<D, 2, KT, 4>(mine, K, Vt, ap.Tp, t0 * KT, T, gw, lane);
+  Pipe<D> pp;
+  {
+    const bf16x8 z = {};
+    pp.pb1[0] = pp.pb1[1] = z;
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) pp.vf.a[gp][db] = z;
+  }
+  __syncthreads();
+  read_k<D, 2, KT>(pp.kf, mine, 0, half, col);
+  qk_qb<D>(pp.s0, st, 0, pp.kf);
+  for (int j = 0; j < nh; ++j) {
+    bf16* cur = mine + (j & 1) * TL::BUF;
+    bf16* nxt = mine + ((j + 1) & 1) * TL::BUF;
+    if (j + 1 < nh) dma_tile<D, 2, KT, 4>(nxt, K, Vt, ap.Tp, (t0 + j + 1) * KT, T, gw, lane);
+    pipe_tile<D, KT>(st, pp, cur, (t0 + j) * KT, T, half, col, j == 0);
+    __syncthreads();  // both halves: tile j+1 is in place, tile j is free
+    if (j + 1 < nh) {
+      read_k<D, 2, KT>(pp.kf, nxt, 0, half, col);
+      qk_qb<D>(pp.s0, st, 0, pp.kf);
+    }
+  }
+  pv_qb<D, 2>(st, 1, pp.pb1, pp.vf);
+
+  // half 1's accumulators, running max and row sums through LDS (register
+  // order: every store and load one row of 64 lanes)
+  float* stt = reinterpret_cast<float*>(lds);
+  constexpr int kO = 2 * (D / 32) * 16;
+  float* my = stt + gw * 64 * (kO + 4);
+  if (hk == 1) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) my[((qb * (D / 32) + db) * 16 + r) * 64 + lane] = st.o[qb][db][r];
+      my[(kO + qb) * 64 + lane] = st.m[qb];
+      my[(kO + 2 + qb) * 64 + lane] = st.l[qb];
+    }
+  }
+  __syncthreads();
+  if (hk == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m1 = my[(kO + qb) * 64 + lane], l1 = my[(kO + 2 + qb) * 64 + lane];
+      const float mx = fmaxf(st.m[qb], m1);
+      const float w0 = __builtin_amdgcn_exp2f(st.m[qb] - mx), w1 = __builtin_amdgcn_exp2f(m1 - mx);
+      st.l[qb] = st.l[qb] * w0 + l1 * w1;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st.o[qb][db][r] =
+              st.o[qb][db][r] * w0 + my[((qb * (D / 32) + db) * 16 + r) * 64 + lane] * w1;
+    }
+    // staging after half 1's state (it is still being read by the other waves)
+    write_o<D, 2>(st, ap, b, head, qbase, half, col, lane,
+                  reinterpret_cast<bf16*>(stt + kState) + gw * 64 * (D + 8));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -812,6 +911,19 @@ void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream
       return;
     }
     if (t256 >= 2 * int64_t(p.cus)) {
+      // whole rounds of two 256-query work-groups per CU; a remainder that
+      // leaves CUs with one work-group runs as split 8-wave work-groups
+      const int64_t slots = 2 * int64_t(p.cus), full = t256 / slots * slots, rest = t256 - full;
+      const int64_t nkt = p.T / 64;
+      if (rest > 0 && rest <= p.cus && p.T % 64 == 0 && nkt % 2 == 0) {
+        typedef Tile<64, 2, 64, 4> TL;
+        ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
+        ap.tile0 = 0;
+        attn2_bf16_kernel<64, 64, 4, 2><<<dim3(unsigned(full)), TL::NTHR, 0, stream>>>(ap);
+        ap.tile0 = int(full);
+        attn2s_bf16_kernel<64, 64><<<dim3(unsigned(rest)), 512, 0, stream>>>(ap);
+        return;
+      }
       launch_bf16_2<64, 64, 4, 2>(ap, bh, stream);
       return;
     }
