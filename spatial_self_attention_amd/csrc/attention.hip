@@ -49,7 +49,6 @@ struct AttnParams {
   void* o;         // (B, T, C)
   int T, Tp, n, d, C;
   int qtiles;      // query tiles per (b, head)
-  int tile0;       // two-block kernels: first (b, head, query tile) of this launch
   float scale;     // log2(e) / sqrt(d) (fp32 path; log2(e) with query/key normalisation)
   const void* rel; // ((2H-1)(2W-1), n) relative-position table, or NULL
   int H, W;
@@ -607,7 +606,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int lid = ap.tile0 + xcd_remap(int(blockIdx.x), int(gridDim.x));
+  const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   const int qtile = lid % ap.qtiles;
   const int bh = lid / ap.qtiles;  // b * n + head
   const int head = bh % ap.n, b = bh / ap.n;
@@ -672,10 +671,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
                 lds + wave * 64 * (D + 8));
 }
 
-// The 256-query tiles of a partial last round: 8 waves, the two halves of the
-// work-group (waves 0-3 and 4-7) taking the same 256 queries against the two
-// halves of the key tiles, each half with its own tile stream, so a CU that
-// would run one 4-wave work-group alone keeps two waves per SIMD.  Half 1
+// 256-query tiles, one per CU: 8 waves, the two halves of the work-group
+// (waves 0-3 and 4-7) taking the same 256 queries against the two halves of
+// the key tiles, each half with its own tile stream (two waves per SIMD, as
+// with two 4-wave work-groups, but a CU finishes one tile at a time).  Half 1
 // leaves (O, m, l) in LDS and half 0 merges:
 //   O = O_0 2^(m_0 - M) + O_1 2^(m_1 - M),  l likewise,  M = max(m_0, m_1).
 // Needs an even number of key tiles, all full.
@@ -692,7 +691,7 @@ __global__ __launch_bounds__(512, 1) void attn2s_bf16_kernel(AttnParams ap) {
   const int half = lane >> 5, col = lane & 31;
   const int hk = __builtin_amdgcn_readfirstlane(wave >> 2);  // key half
   const int gw = __builtin_amdgcn_readfirstlane(wave & 3);   // wave within the half
-  const int lid = ap.tile0 + xcd_remap(int(blockIdx.x), int(gridDim.x));
+  const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   const int qtile = lid % ap.qtiles;
   const int bh = lid / ap.qtiles;
   const int head = bh % ap.n, b = bh / ap.n;
@@ -899,8 +898,9 @@ void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
 // kernel reads half the LDS operand bytes per MFMA but holds twice the
 // queries per wave, so it needs whole rounds of work-groups to pay.  512-query
 // work-groups (8 waves, key tiles of 128, one per CU) when the query tiles
-// fill whole rounds of the CUs or many of them; 256-query work-groups (4
-// waves, key tiles of 64, two per CU) when they fill at least one round;
+// fill whole rounds of the CUs or many of them; 256-query tiles (key tiles of
+// 64: one 8-wave key-splitting work-group or two 4-wave work-groups per CU)
+// when they fill at least one round of two per CU;
 // otherwise (shorter or fewer sequences) the one-block kernel, whose
 // 128-query work-groups spread the work more evenly.
 void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream) {
@@ -911,17 +911,14 @@ void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream
       return;
     }
     if (t256 >= 2 * int64_t(p.cus)) {
-      // whole rounds of two 256-query work-groups per CU; a remainder that
-      // leaves CUs with one work-group runs as split 8-wave work-groups
-      const int64_t slots = 2 * int64_t(p.cus), full = t256 / slots * slots, rest = t256 - full;
-      const int64_t nkt = p.T / 64;
-      if (rest > 0 && rest <= p.cus && p.T % 64 == 0 && nkt % 2 == 0) {
+      // 256-query tiles.  With an even number of full key tiles each tile runs
+      // as one 8-wave work-group whose halves split the keys: faster per tile
+      // than two 4-wave work-groups sharing a CU, and a partial last round is
+      // then a round of whole CUs; otherwise two 4-wave work-groups per CU.
+      if (p.T % 128 == 0) {
         typedef Tile<64, 2, 64, 4> TL;
         ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
-        ap.tile0 = 0;
-        attn2_bf16_kernel<64, 64, 4, 2><<<dim3(unsigned(full)), TL::NTHR, 0, stream>>>(ap);
-        ap.tile0 = int(full);
-        attn2s_bf16_kernel<64, 64><<<dim3(unsigned(rest)), 512, 0, stream>>>(ap);
+        attn2s_bf16_kernel<64, 64><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
         return;
       }
       launch_bf16_2<64, 64, 4, 2>(ap, bh, stream);

@@ -1,8 +1,9 @@
 """The attention stage alone on long sequences (bf16, d = 64, T >= 1024),
 covering each kernel shape the stage picks there: the two-query-block kernel
 with 512-query work-groups (key tiles of 128) or 256-query work-groups (key
-tiles of 64, a partial last round of them as 8-wave work-groups that split
-the keys in halves and merge in LDS), and the one-block kernel when the query
+tiles of 64: 8-wave work-groups that split the keys in halves and merge in
+LDS when the sequence is a multiple of 128 (T = 9216, 8320), two 4-wave
+work-groups per CU otherwise (T = 9215, 9280)), and the one-block kernel when the query
 tiles are too few to fill whole rounds of the CUs (the choice assumes
 MI355X's 256 CUs).
 
@@ -75,9 +76,10 @@ CASES = [
     (1, 32, 63, 63, 40),      # 256 query tiles of 512: T % 128 = 1, last tile 385 rows
     (2, 16, 64, 64, 48),      # 256 query tiles of 512, even sizes
     (2, 10, 95, 97, 40),      # 720 query tiles of 256: T % 64 = 63
-    (2, 10, 96, 96, 40),      # the high-resolution workload's shape: tiles of 256 (512 in
-                              # whole rounds, the other 208 split over the keys)
-    (2, 10, 80, 104, 40),     # 660 tiles of 256 (148 split), the last one 128 rows
+    (2, 10, 96, 96, 40),      # the high-resolution workload's shape: 720 tiles of 256, each
+                              # split over the keys by the halves of one work-group
+    (2, 10, 80, 104, 40),     # 660 such tiles, the last one of each head 128 rows
+    (2, 10, 80, 116, 40),     # T % 128 = 64: two 4-wave work-groups per CU, full key tiles
 ]
 
 
