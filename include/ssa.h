@@ -38,24 +38,34 @@
  *   error nothing is launched and nothing is written.
  * - B == 0, H == 0 or W == 0 is an empty input: SSA_OK, nothing launched, and
  *   the data pointers may be NULL.
- * - Supported: fp32 with 1 <= d <= 128; bf16 (fp32 accumulation) with
- *   d in {32, 64, 96, 128}.  Other head sizes return SSA_E_UNSUPPORTED, and
- *   so does a call with 3*B*H*W*C >= 2^31 (the Q|K|V projection's output
- *   must stay below 2^31 elements; every tensor then fits 32-bit offsets).
+ * - Supported: fp32 and bf16 (fp32 accumulation) with 1 <= d <= 128.  A
+ *   head size above 128 returns SSA_E_UNSUPPORTED, and so does a call with
+ *   3*B*H*W*C >= 2^31 (the Q|K|V projection's output must stay below 2^31
+ *   elements; every tensor then fits 32-bit offsets).  bf16 heads narrower
+ *   than a multiple of 32 are zero-padded to the next one (dp below), which
+ *   leaves every score and output unchanged.
  *
  * Workspace (bytes from ssa_workspace_size; regions from
  * ssa_get_workspace_layout, each 256-byte aligned):
  *   gn_partial  float4 (count, mean, M2, 0) per (b, g, split)
  *   gn_stats    float2 (mean, rstd) per (b, g)
  *   gn_coef     float2 (a, s) per (b, c): GN(x)[b,c,t] = a*x[b,c,t] + s
- *   q, k        (B, n, T, d)   dtype, token-major per head; bf16 q holds
- *                              Q * log2(e) / sqrt(d) (the score scale)
- *   vt          (B, n, d, Tp)  dtype, V transposed, Tp = T rounded up to 64;
+ *   q, k        (B, n, T, dp)  dtype, token-major per head; dp = d for fp32,
+ *                              d rounded up to a multiple of 32 for bf16, the
+ *                              columns d .. dp-1 zero; bf16 q holds
+ *                              Q * log2(e) / sqrt(d) (the score scale; with
+ *                              query/key normalisation Q * log2(e))
+ *   vt          (B, n, dp, Tp) dtype, V transposed, Tp = T rounded up to 64;
  *                              fp32: token t in column t; bf16: token t in
  *                              column t with bits 2 and 3 swapped (the order of
  *                              the attention kernel's MFMA operand); columns of
- *                              tokens >= T are never written
+ *                              tokens >= T and rows d .. dp-1 are never written
  *   o           (B, T, C)      dtype, heads concatenated along channels
+ *   rope        (T, d/2) float2 (cos, sin) of the rotary angles (bf16 with
+ *                              d in {16, 32, 64, 128} and the projection's main
+ *                              path: C % 64 == 0, T % 4 == 0); else empty
+ *   qk32        (2, B, n, T, d) fp32 Q and K before the optional steps (bf16
+ *                              problems without the rope region); else empty
  * After ssa_forward these hold the block's intermediates for inspection.
  */
 #ifndef SSA_H_
@@ -106,8 +116,11 @@ typedef struct {
   size_t k;
   size_t vt;
   size_t o;
+  size_t rope;         /* 0 bytes long when absent (offset of the next region) */
+  size_t qk32;
   int64_t gn_splits;   /* splits per (b, g) segment in gn_partial             */
   int64_t t_pad;       /* Tp: row pitch of vt in elements                     */
+  int64_t d_pad;       /* dp: row pitch of q and k, rows per head of vt       */
 } ssa_workspace_layout;
 
 /* Bytes of workspace ssa_forward needs for this problem, or 0 when the
@@ -193,6 +206,24 @@ ssa_status ssa_forward_ex(const void* x, void* out,
                           int64_t num_groups, int64_t num_heads, int dtype,
                           const ssa_options* options,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssa_forward_stage with optional steps (options may be NULL): one stage of
+ * ssa_forward_ex.  Running stages 0, 1, 2, 3 in order on one stream with one
+ * workspace and the same options is exactly ssa_forward_ex (which never runs
+ * the fused stage 4 while an optional step is on; stage 4 with an optional
+ * step on returns SSA_E_UNSUPPORTED).  Used to time and inspect the kernels of
+ * the optional steps. */
+ssa_status ssa_forward_stage_ex(int stage,
+                                const void* x, void* out,
+                                const void* norm_weight, const void* norm_bias,
+                                const void* q_weight, const void* k_weight,
+                                const void* v_weight, const void* out_weight,
+                                const void* q_bias, const void* k_bias,
+                                const void* v_bias, const void* out_bias,
+                                int64_t B, int64_t C, int64_t H, int64_t W,
+                                int64_t num_groups, int64_t num_heads, int dtype,
+                                const ssa_options* options,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* 1 when ssa_forward (and ssa_forward_ex with no optional step on) runs the
  * fused stage SSA_STAGE_QKV_ATTENTION for this problem, else 0 (also for

@@ -16,8 +16,8 @@ import torch
 
 from ._binding import (  # noqa: F401
     BIAS_KEYS, EXPORTS, LIB_PATH, PARAM_ORDER, SSA_BF16, SSA_F32, STAGES, Options, SSAError,
-    SSAValueError, lib, ssa_forward, ssa_forward_ex, ssa_forward_stage, ssa_get_workspace_layout,
-    ssa_status_string, ssa_uses_fused_stage, ssa_workspace_size,
+    SSAValueError, lib, ssa_forward, ssa_forward_ex, ssa_forward_stage, ssa_forward_stage_ex,
+    ssa_get_workspace_layout, ssa_status_string, ssa_uses_fused_stage, ssa_workspace_size,
 )
 from ._binding import _raise
 
@@ -87,10 +87,12 @@ def make_options(x, num_heads, rel_pos_table=None, q_norm_gamma=None, k_norm_gam
     return Options(_ptr(rel_pos_table), _ptr(q_norm_gamma), _ptr(k_norm_gamma), 1 if rope else 0)
 
 
-def forward_stages(x, num_groups: int, num_heads: int) -> tuple:
-    """The stage names ssa_forward runs for x's problem, in order."""
+def forward_stages(x, num_groups: int, num_heads: int, options=None) -> tuple:
+    """The stage names ssa_forward (ssa_forward_ex with `options`) runs for
+    x's problem, in order."""
     B, C, H, W = x.shape
-    if ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads, dtype_code(x.dtype)):
+    if options is None and ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads,
+                                                dtype_code(x.dtype)):
         return ("gn_stats", "qkv_attention", "out_proj")
     return ("gn_stats", "qkv", "attention", "out_proj")
 
@@ -107,9 +109,10 @@ def forward_into(x, params, num_groups, num_heads, out, workspace, stage=None,
     ptrs = [_ptr(params[k]) for k in PARAM_ORDER]
     head = (_ptr(x), _ptr(out), ptrs, B, C, H, W, num_groups, num_heads, dtype_code(x.dtype))
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), stream.cuda_stream)
-    if stage is not None:
-        if options is not None:
-            raise ValueError("stages run the plain block; options need the whole call")
+    if stage is not None and options is not None:
+        _raise(ssa_forward_stage_ex(STAGES.get(stage, stage), *head, options, *tail),
+               "ssa_forward_stage_ex")
+    elif stage is not None:
         _raise(ssa_forward_stage(STAGES.get(stage, stage), *head, *tail), "ssa_forward_stage")
     elif options is not None:
         _raise(ssa_forward_ex(*head, options, *tail), "ssa_forward_ex")

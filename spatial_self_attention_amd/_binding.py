@@ -29,7 +29,8 @@ PARAM_ORDER = (
 )
 
 EXPORTS = ("ssa_workspace_size", "ssa_get_workspace_layout", "ssa_forward",
-           "ssa_forward_ex", "ssa_forward_stage", "ssa_uses_fused_stage", "ssa_status_string")
+           "ssa_forward_ex", "ssa_forward_stage", "ssa_forward_stage_ex", "ssa_uses_fused_stage",
+           "ssa_status_string")
 
 BIAS_KEYS = ("q_bias", "k_bias", "v_bias", "out_bias")
 
@@ -54,8 +55,11 @@ class WorkspaceLayout(ctypes.Structure):
         ("k", ctypes.c_size_t),
         ("vt", ctypes.c_size_t),
         ("o", ctypes.c_size_t),
+        ("rope", ctypes.c_size_t),
+        ("qk32", ctypes.c_size_t),
         ("gn_splits", ctypes.c_int64),
         ("t_pad", ctypes.c_int64),
+        ("d_pad", ctypes.c_int64),
     ]
 
 
@@ -94,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.ssa_forward_stage.argtypes = [ctypes.c_int] + fwd
     L.ssa_forward_ex.restype = ctypes.c_int
     L.ssa_forward_ex.argtypes = fwd[:19] + [ctypes.POINTER(Options)] + fwd[19:]
+    L.ssa_forward_stage_ex.restype = ctypes.c_int
+    L.ssa_forward_stage_ex.argtypes = [ctypes.c_int] + fwd[:19] + [ctypes.POINTER(Options)] + fwd[19:]
     L.ssa_uses_fused_stage.restype = ctypes.c_int
     L.ssa_uses_fused_stage.argtypes = [i64] * 6 + [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -152,6 +158,15 @@ def ssa_forward_stage(stage, x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups,
     return int(lib().ssa_forward_stage(int(stage), x_ptr, out_ptr, *param_ptrs, B, C, H, W,
                                        num_groups, num_heads, int(dtype), ws_ptr, ws_bytes,
                                        stream_ptr))
+
+
+def ssa_forward_stage_ex(stage, x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups, num_heads,
+                         dtype, options, ws_ptr, ws_bytes, stream_ptr) -> int:
+    """Raw call of one stage with an Options structure (or None)."""
+    opt = ctypes.byref(options) if options is not None else None
+    return int(lib().ssa_forward_stage_ex(int(stage), x_ptr, out_ptr, *param_ptrs, B, C, H, W,
+                                          num_groups, num_heads, int(dtype), opt, ws_ptr,
+                                          ws_bytes, stream_ptr))
 
 
 def ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads, dtype) -> bool:

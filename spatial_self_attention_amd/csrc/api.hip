@@ -29,10 +29,9 @@ int device_cus() {
   return cache[dev];
 }
 
-bool supported_head(int dtype, int64_t d) {
-  if (dtype == SSA_F32) return d >= 1 && d <= 128;
-  return d == 32 || d == 64 || d == 96 || d == 128;
-}
+// Every head size up to 128, in both dtypes (bf16 heads are zero-padded to a
+// multiple of 32, the widths of the attention kernels' MFMA operands).
+bool supported_head(int64_t d) { return d >= 1 && d <= 128; }
 
 // Size checks shared by every entry point.  On success fills *p (when the
 // input is non-empty) and sets *empty.
@@ -42,7 +41,7 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
   if (B < 0 || H < 0 || W < 0 || C < 1) return SSA_E_SHAPE;
   if (G < 1 || n < 1 || C % G != 0 || C % n != 0) return SSA_E_CONSTRAINT;
   const int64_t d = C / n;
-  if (!supported_head(dtype, d)) return SSA_E_UNSUPPORTED;
+  if (!supported_head(d)) return SSA_E_UNSUPPORTED;
   *empty = (B == 0 || H == 0 || W == 0);
   if (*empty) return SSA_OK;
   const int64_t T = H * W;
@@ -54,7 +53,10 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
   p->Tp = (T + kTokPad - 1) / kTokPad * kTokPad;
   p->dtype = dtype;
   p->esize = dtype == SSA_F32 ? 4 : 2;
+  p->dp = dtype == SSA_F32 ? d : (d + 31) / 32 * 32;
   p->cus = device_cus();
+  p->qkv_main = dtype == SSA_BF16 && C % 64 == 0 && T % 4 == 0 && d % 8 == 0;
+  p->qk_fuse = p->qkv_main && (d == 16 || d == 32 || d == 64 || d == 128);
 
   // Statistics split.  With enough (b, g) segments to fill the chip and
   // segments a work-group streams quickly, one work-group per segment also
@@ -85,13 +87,21 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
   ws.gn_stats = take(size_t(segs) * 8);
   ws.gn_coef = take(size_t(B * C) * 8);
   const size_t e = p->esize;
-  ws.q = take(size_t(B * n * T * d) * e);
-  ws.k = take(size_t(B * n * T * d) * e);
-  ws.vt = take(size_t(B * n * d * p->Tp) * e);
+  const int64_t dp = p->dp;
+  ws.q = take(size_t(B * n * T * dp) * e);
+  ws.k = take(size_t(B * n * T * dp) * e);
+  ws.vt = take(size_t(B * n * dp * p->Tp) * e);
   ws.o = take(size_t(B * T * C) * e);
+  // The optional query/key steps' buffers are sized from the problem alone
+  // (ssa_workspace_size does not see the options): the rotary table where the
+  // projection epilogue applies the steps, else fp32 Q and K for the pass
+  // that does (bf16 only: fp32 Q and K are written unrounded anyway).
+  ws.rope = take(p->qk_fuse ? size_t(T * (d / 2)) * 8 : 0);
+  ws.qk32 = take(dtype == SSA_BF16 && !p->qk_fuse ? size_t(2 * B * T * C) * 4 : 0);
   ws.total = off;
   ws.gn_splits = p->splits;
   ws.t_pad = p->Tp;
+  ws.d_pad = dp;
   return SSA_OK;
 }
 
@@ -172,7 +182,8 @@ ssa_status run(int stage, const void* x, void* out, const void* nw, const void* 
   int stages[4] = {SSA_STAGE_GN_STATS, SSA_STAGE_QKV, SSA_STAGE_ATTENTION, SSA_STAGE_OUT_PROJ};
   int count = 4;
   if (stage >= 0) {
-    if (stage == SSA_STAGE_QKV_ATTENTION && !fused_available(p)) return SSA_E_UNSUPPORTED;
+    if (stage == SSA_STAGE_QKV_ATTENTION && (!fused_available(p) || !plain))
+      return SSA_E_UNSUPPORTED;
     stages[0] = stage;
     count = 1;
   } else if (plain && fused_available(p)) {
@@ -184,10 +195,14 @@ ssa_status run(int stage, const void* x, void* out, const void* nw, const void* 
     hipError_t e = hipSuccess;
     switch (stages[i]) {
       case SSA_STAGE_GN_STATS: e = launch_gn_stats(p, a); break;
-      case SSA_STAGE_QKV:
-        e = launch_qkv_proj(p, a);
-        if (e == hipSuccess && (a.rope || a.q_norm_gamma != nullptr)) e = launch_qk_post(p, a);
+      case SSA_STAGE_QKV: {
+        const bool qk_opt = a.rope || a.q_norm_gamma != nullptr;
+        if (p.dp > p.d) e = launch_zero_pad(p, a);
+        if (e == hipSuccess && qk_opt && a.rope && p.qk_fuse) e = launch_rope_table(p, a);
+        if (e == hipSuccess) e = launch_qkv_proj(p, a);
+        if (e == hipSuccess && qk_opt && !p.qk_fuse) e = launch_qk_post(p, a);
         break;
+      }
       case SSA_STAGE_ATTENTION: e = launch_attention(p, a); break;
       case SSA_STAGE_OUT_PROJ: e = launch_out_proj(p, a); break;
       case SSA_STAGE_QKV_ATTENTION: e = launch_fused(p, a); break;
@@ -259,6 +274,19 @@ ssa_status ssa_forward_stage(int stage, const void* x, void* out, const void* no
                   num_heads, dtype, nullptr, workspace, workspace_bytes, stream);
 }
 
+ssa_status ssa_forward_stage_ex(int stage, const void* x, void* out, const void* norm_weight,
+                                const void* norm_bias, const void* q_weight, const void* k_weight,
+                                const void* v_weight, const void* out_weight, const void* q_bias,
+                                const void* k_bias, const void* v_bias, const void* out_bias,
+                                int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
+                                int64_t num_heads, int dtype, const ssa_options* options,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < SSA_STAGE_GN_STATS || stage > SSA_STAGE_QKV_ATTENTION) return SSA_E_STAGE;
+  return ssa::run(stage, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight,
+                  out_weight, q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups,
+                  num_heads, dtype, options, workspace, workspace_bytes, stream);
+}
+
 int ssa_uses_fused_stage(int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
                          int64_t num_heads, int dtype) {
   ssa::Plan p;
@@ -278,9 +306,8 @@ const char* ssa_status_string(int status) {
              "come together";
     case SSA_E_DTYPE: return "unknown dtype";
     case SSA_E_UNSUPPORTED:
-      return "unsupported size: head size must be 1..128 (fp32) or 32/64/96/128 (bf16), even "
-             "with rotary embeddings, and 3*B*H*W*C below 2^31; the fused stage only where "
-             "ssa_uses_fused_stage() is 1";
+      return "unsupported size: head size must be 1..128, even with rotary embeddings, and "
+             "3*B*H*W*C below 2^31; the fused stage only where ssa_uses_fused_stage() is 1";
     case SSA_E_WORKSPACE: return "workspace smaller than ssa_workspace_size()";
     case SSA_E_ALIAS: return "out or workspace overlaps another buffer";
     case SSA_E_ALIGN: return "a pointer is not 16-byte aligned";

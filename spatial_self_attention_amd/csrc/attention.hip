@@ -43,11 +43,11 @@ namespace ssa {
 namespace {
 
 struct AttnParams {
-  const void* q;   // (B, n, T, d)
-  const void* k;   // (B, n, T, d)
-  const void* vt;  // (B, n, d, Tp)
+  const void* q;   // (B, n, T, dp)
+  const void* k;   // (B, n, T, dp)
+  const void* vt;  // (B, n, dp, Tp)
   void* o;         // (B, T, C)
-  int T, Tp, n, d, C;
+  int T, Tp, n, d, C;  // d: the head's width (bf16 kernels run at D = dp >= d)
   int qtiles;      // query tiles per (b, head)
   float scale;     // log2(e) / sqrt(d) (fp32 path; log2(e) with query/key normalisation)
   const void* rel; // ((2H-1)(2W-1), n) relative-position table, or NULL
@@ -304,15 +304,28 @@ __device__ __forceinline__ void write_o(const AttnState<D, QB>& st, const AttnPa
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   constexpr int CPR = D / 8;  // 16-byte chunks per query row
-  bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * ap.T) * ap.C + head * D;
+  // a head of d < D channels (zero-padded operands): its first d columns
+  const int d = ap.d;
+  bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * ap.T) * ap.C + head * d;
+  if (d == D) {
 #pragma unroll
-  for (int i = 0; i < QB * D / 16; ++i) {
-    const int c = lane + 64 * i;
-    const int q = c / CPR, dc = c % CPR;
-    const int qi = qbase + q;
-    if (qi < ap.T)
-      *reinterpret_cast<bf16x8*>(O + int64_t(qi) * ap.C + dc * 8) =
-          *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]);
+    for (int i = 0; i < QB * D / 16; ++i) {
+      const int c = lane + 64 * i;
+      const int q = c / CPR, dc = c % CPR;
+      const int qi = qbase + q;
+      if (qi < ap.T)
+        *reinterpret_cast<bf16x8*>(O + int64_t(qi) * ap.C + dc * 8) =
+            *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]);
+    }
+  } else {
+    for (int i = 0; i < QB * D / 16; ++i) {
+      const int c = lane + 64 * i;
+      const int q = c / CPR, dc = c % CPR;
+      const int qi = qbase + q;
+      if (qi < ap.T && dc * 8 < d)
+        for (int e = 0; e < 8 && dc * 8 + e < d; ++e)
+          O[int64_t(qi) * ap.C + dc * 8 + e] = stg[q * EP + dc * 8 + e];
+    }
   }
 }
 
@@ -937,6 +950,8 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   ap.vt = a.ws + p.ws.vt;
   ap.o = a.ws + p.ws.o;
   ap.T = int(p.T);
+  // bf16 kernels run at the padded width dp (q, k zero past d); d is the
+  // head's own width (score scale, output columns)
   ap.Tp = int(p.Tp);
   ap.n = int(p.n);
   ap.d = int(p.d);
@@ -951,7 +966,7 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   if (p.dtype == SSA_BF16) {
     // one 256-query work-group per head when the heads alone fill the chip
     const bool wide = p.T <= 256 && bh >= p.cus;
-    switch (p.d) {
+    switch (p.dp) {
       case 32: launch_bf16<32, 1, 64, 4>(ap, bh, a.stream); break;
       case 64:
         if (wide) launch_bf16<64, 1, 64, 8>(ap, bh, a.stream);

@@ -43,10 +43,19 @@ struct ProjParams {
   void* vt;            // (B, n, d, Tp)
   void* out;           // (B, C, T) (kOut)
   int C, T, n, d, Tp;
+  int dp;              // head width of the q / k / vt layouts (bf16: d rounded up to 32)
   int M;               // 3C (kQkv) or C (kOut)
   float q_scale;       // bf16 Q is stored times log2(e) / sqrt(d) (kQkv)
   int64_t NT;          // B*T tokens
+  // optional query/key steps (kQkv, bf16)
+  const void* gq;      // (n, d) query / key normalisation gammas, or NULL
+  const void* gk;
+  int rope;            // rotary embedding on
+  const float2* rope_tab;  // (T, d/2) (cos, sin) of the rotary angles
+  float* qk32;         // (2, B, n, T, d) fp32 Q and K for the separate option pass, or NULL
 };
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernels
@@ -54,8 +63,10 @@ struct ProjParams {
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDP = BK + 8;  // LDS row pitch (bf16): 144 B rows spread the banks
 
-// Quad-token loads need T % 4 == 0 (a quad never straddles two samples).
-template <int MODE, bool QUAD>
+// Quad-token loads need T % 4 == 0 (a quad never straddles two samples);
+// V8: C % 8 == 0, so every 8-channel vector that starts inside a row ends
+// inside it (otherwise the loads go element by element).
+template <int MODE, bool QUAD, bool V8>
 __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
   __shared__ __attribute__((aligned(16))) bf16 As[BM * LDP];
   __shared__ __attribute__((aligned(16))) bf16 Bs[BN * LDP];
@@ -87,8 +98,14 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
       if (m < pp.M && k < C) {
         const int which = MODE == kQkv ? m / C : 0;
         const int row = MODE == kQkv ? m - which * C : m;
-        const bf16* w = static_cast<const bf16*>(pp.w[which]);
-        ra[i] = *reinterpret_cast<const bf16x8*>(w + int64_t(row) * C + k);
+        const bf16* w = static_cast<const bf16*>(pp.w[which]) + int64_t(row) * C + k;
+        if (V8) {
+          ra[i] = *reinterpret_cast<const bf16x8*>(w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k + e < C) ra[i][e] = w[e];
+        }
       }
     }
     // ---- B: 128 tokens x 64 channels ----
@@ -101,7 +118,15 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
         const int64_t nn = n0 + r;
         const int k = k0 + (tid & 7) * 8;
         rb[i] = zero8;
-        if (nn < pp.NT && k < C) rb[i] = *reinterpret_cast<const bf16x8*>(o + nn * C + k);
+        if (nn < pp.NT && k < C) {
+          if (V8) {
+            rb[i] = *reinterpret_cast<const bf16x8*>(o + nn * C + k);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (k + e < C) rb[i][e] = o[nn * C + k + e];
+          }
+        }
       }
     } else {
       // thread = (token quad tq, channel octet co); rb[tok] = 8 channels of token tok
@@ -118,6 +143,11 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
           const float2* cf = pp.coef + b * C + kb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
+            if (!V8 && kb + j >= C) {  // channels past C: zero operand columns
+#pragma unroll
+              for (int e = 0; e < 4; ++e) z[e][j] = 0.f;
+              continue;
+            }
             const bf16x4 v = *reinterpret_cast<const bf16x4*>(xp + int64_t(j) * T);
             const float2 ab = cf[j];
 #pragma unroll
@@ -140,7 +170,8 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
             const float2* cf = pp.coef + b * C + kb;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-              z[e][j] = cf[j].x * static_cast<float>(xp[int64_t(j) * T]) + cf[j].y;
+              z[e][j] = (V8 || kb + j < C) ? cf[j].x * static_cast<float>(xp[int64_t(j) * T]) + cf[j].y
+                                           : 0.f;
           } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) z[e][j] = 0.f;
@@ -205,35 +236,40 @@ __global__ __launch_bounds__(256) void proj_bf16_kernel(ProjParams pp) {
       for (int g = 0; g < 4; ++g) {
         const int m = m0 + wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5);
         if (m >= pp.M) continue;
-        const int which = MODE == kQkv ? m / C : 0;
-        const int c = m - which * C;
-        const bf16* bias = static_cast<const bf16*>(pp.bias[which]);  // NULL: no bias
         float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = acc[i][j][4 * g + e] + (bias ? static_cast<float>(bias[c + e]) : 0.f);
         if constexpr (MODE == kQkv) {
-          const int head = c / pp.d, dd = c - head * pp.d;
-          const int64_t bh = b * pp.n + head;
-          if (which < 2) {
-            const float sc = which == 0 ? pp.q_scale : 1.f;
-            bf16x4 pk;
+          // element by element: any C, so the 4 rows may straddle Q / K / V and
+          // heads of any size
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(v[e] * sc);
-            bf16* dst = static_cast<bf16*>(which == 0 ? pp.q : pp.k);
-            *reinterpret_cast<bf16x4*>(dst + (bh * T + t) * pp.d + dd) = pk;
-          } else {
-            bf16* dst = static_cast<bf16*>(pp.vt);
-            const int slot = vt_slot(t);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dst[(bh * pp.d + dd + e) * pp.Tp + slot] = static_cast<bf16>(v[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int me = m + e;
+            if (me >= pp.M) break;
+            const int which = me / C;
+            const int c = me - which * C;
+            const bf16* bias = static_cast<const bf16*>(pp.bias[which]);  // NULL: no bias
+            const float val = acc[i][j][4 * g + e] + (bias ? static_cast<float>(bias[c]) : 0.f);
+            const int head = c / pp.d, dd = c - head * pp.d;
+            const int64_t bh = b * pp.n + head;
+            if (which < 2 && pp.qk32 != nullptr) {  // fp32 for the separate option pass
+              pp.qk32[(int64_t(which) * pp.NT * pp.n + bh * T + t) * pp.d + dd] = val;
+            } else if (which < 2) {
+              bf16* dst = static_cast<bf16*>(which == 0 ? pp.q : pp.k);
+              dst[(bh * T + t) * pp.dp + dd] = static_cast<bf16>(val * (which == 0 ? pp.q_scale : 1.f));
+            } else {
+              static_cast<bf16*>(pp.vt)[(bh * pp.dp + dd) * pp.Tp + vt_slot(t)] = static_cast<bf16>(val);
+            }
           }
         } else {
+          const bf16* bias = static_cast<const bf16*>(pp.bias[0]);  // NULL: no bias
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = acc[i][j][4 * g + e] + (bias && m + e < C ? static_cast<float>(bias[m + e]) : 0.f);
+          const int c = m;
           const bf16* x = static_cast<const bf16*>(pp.x);
           bf16* out = static_cast<bf16*>(pp.out);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            if (c + e >= C) break;
             const int64_t idx = (b * C + c + e) * T + t;
             out[idx] = static_cast<bf16>(static_cast<float>(x[idx]) + v[e]);
           }
@@ -605,11 +641,29 @@ __device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], EpiPre& ep, const
   }
 }
 
-template <int MODE, bool TR>
+template <int MODE, bool TR, int QKO>
 __device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const EpiPre& ep,
                                           const ProjParams& pp, bf16* stg, const EpiCtx& ec) {
   const int C = pp.C, half = ec.half, col = ec.col;
-  if constexpr (MODE == kOut) {
+  if constexpr (MODE == kQkv && !TR && QKO != 0) {
+    // Q or K with an optional step: acc + bias in fp32, token-major, so that
+    // the steps run on unrounded values and Q and K are rounded once
+    float* E = reinterpret_cast<float*>(stg);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cl = i * 32 + 8 * g + 4 * half;
+        const bf16x4 bv = ep.qk_bias[i][g];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + static_cast<float>(bv[e]);
+          *reinterpret_cast<f32x4*>(&E[(j * 32 + col) * EPF + cl]) = v;
+        }
+      }
+  } else if constexpr (MODE == kOut) {
     float* E = reinterpret_cast<float*>(stg);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -660,6 +714,131 @@ __device__ __forceinline__ void epi_stage(const f32x16 (&acc)[2][2], const EpiPr
   }
 }
 
+// The staging region of wave w (its 64 x 64 quadrant, fp32 or bf16).
+__device__ __forceinline__ bf16* stage_region(bf16* lds0, bf16* lds1, int w) {
+  return (w < 2 ? lds0 : lds1) + (w & 1) * 64 * EPF * 2;
+}
+
+// Query/key normalisation and rotary embedding in the Q / K epilogue
+// (d in {16, 32, 64, 128}; vit-pytorch simple_vit_with_qk_norm.py, RMSNorm:
+// x / max(||x||, 1e-12) * sqrt(d) * gamma; HNDL attention operator, "Rotary
+// embeddings": rotate-half, element i paired with i + d/2), from acc + bias
+// staged in fp32 by every wave.  A lane takes 4 items (token, head, chunk ic
+// of 8 element pairs) of its wave's 64 x 64 quadrant; with d = 128 a head's
+// two halves lie in the quadrants of waves (0, wn) and (1, wn), which then
+// take 32 tokens each.  The d/16 lanes of one (token, head) are consecutive,
+// so the squared norm is summed with lane shuffles.  The rotation's (cos,
+// sin) come from the per-call table (float32 angle t * theta_i).  Q and K are
+// rounded to bf16 once; Q is stored times log2(e) (normalised: its scores are
+// not divided by sqrt(d)) or times log2(e)/sqrt(d).
+__device__ __forceinline__ void epi_store_qkopt(const ProjParams& pp, bf16* lds0, bf16* lds1,
+                                                const EpiCtx& ec, int wave) {
+  const int d = pp.d, C = pp.C, T = pp.T, lane = ec.lane;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int which = ec.mw / C;                  // 0: Q, 1: K (V waves never come here)
+  const int lg = d == 16 ? 0 : d == 32 ? 1 : d == 64 ? 2 : 3;  // log2(d / 16)
+  const int nic = 1 << lg;                      // chunks of 8 pairs per head
+  const bool wide = d == 128;
+  const int lh = wide ? 0 : 2 - lg;             // log2(heads per quadrant)
+  const int head0 = ((wide ? ec.mw - 64 * wm : ec.mw) - which * C) / d;
+  const float* Ra = reinterpret_cast<const float*>(stage_region(lds0, lds1, (wide ? 0 : wm) * 2 + wn));
+  const float* Rb = reinterpret_cast<const float*>(stage_region(lds0, lds1, (wide ? 1 : wm) * 2 + wn));
+  const int ic = lane & (nic - 1);
+  const bf16* gam = static_cast<const bf16*>(which == 0 ? pp.gq : pp.gk);
+  const float sc = which == 0 ? (gam != nullptr ? kLog2e : pp.q_scale) : 1.f;
+  bf16* dst = static_cast<bf16*>(which == 0 ? pp.q : pp.k);
+  const float sqd = sqrtf(float(d));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rest = (lane + 64 * u) >> lg;
+    const int hs = rest & ((1 << lh) - 1);
+    const int tl = (wide ? 32 * wm : 0) + (rest >> lh);
+    const int ca = hs * d + ic * 8;             // a-run in Ra (first half of the head)
+    const int cb = wide ? ic * 8 : ca + d / 2;  // b-run in Rb (second half)
+    float a[8], b[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 va = *reinterpret_cast<const f32x4*>(&Ra[tl * EPF + ca + 4 * h]);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(&Rb[tl * EPF + cb + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[4 * h + e] = va[e];
+        b[4 * h + e] = vb[e];
+      }
+    }
+    const int head = head0 + hs;
+    const int nn = ec.nw + tl;
+    const int nc = min(nn, int(pp.NT) - 1);   // rows past the last token: any valid one
+    const int bs = int(unsigned(nc) / unsigned(T)), t = nc - bs * T;
+    if (gam != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += a[e] * a[e] + b[e] * b[e];
+      for (int m = 1; m < nic; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      const float f = sqd / fmaxf(sqrtf(ss), 1e-12f);
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gam + head * d + ic * 8);
+      const bf16x8 gb = *reinterpret_cast<const bf16x8*>(gam + head * d + d / 2 + ic * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] *= f * static_cast<float>(ga[e]);
+        b[e] *= f * static_cast<float>(gb[e]);
+      }
+    }
+    if (pp.rope) {
+      const f32x4* rt = reinterpret_cast<const f32x4*>(pp.rope_tab + int64_t(t) * (d / 2) + ic * 8);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f32x4 cs = rt[h];  // (cos, sin) of pairs 2h and 2h + 1 of the chunk
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float c = cs[2 * e], sn = cs[2 * e + 1];
+          const float na = a[2 * h + e] * c - b[2 * h + e] * sn;
+          const float nb = b[2 * h + e] * c + a[2 * h + e] * sn;
+          a[2 * h + e] = na;
+          b[2 * h + e] = nb;
+        }
+      }
+    }
+    if (nn < pp.NT) {
+      bf16x8 pa, pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pa[e] = static_cast<bf16>(a[e] * sc);
+        pb[e] = static_cast<bf16>(b[e] * sc);
+      }
+      bf16* row = dst + (int64_t(bs * pp.n + head) * T + t) * pp.dp;
+      *reinterpret_cast<bf16x8*>(row + ic * 8) = pa;
+      *reinterpret_cast<bf16x8*>(row + d / 2 + ic * 8) = pb;
+    }
+  }
+}
+
+// Q or K in fp32 (acc + bias, unscaled) into the qk32 region, for the separate
+// pass of the optional steps (head sizes the fused epilogue does not take):
+// lane (8-channel run q8, tokens r0 + 8u), d % 8 == 0 keeps a run in one head.
+__device__ __forceinline__ void epi_store_qk32(const ProjParams& pp, const bf16* stg,
+                                               const EpiCtx& ec) {
+  const int C = pp.C, T = pp.T, lane = ec.lane;
+  const float* E = reinterpret_cast<const float*>(stg);
+  const int which = ec.mw / C;
+  float* dst = pp.qk32 + int64_t(which) * pp.NT * C;
+  const int q8 = lane & 7;
+  const int c = ec.mw - which * C + q8 * 8;
+  const int head = int(unsigned(c) / unsigned(pp.d)), dd = c - head * pp.d;
+  const int r0 = lane >> 3;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int nn = ec.nw + r0 + 8 * u;
+    if (nn >= pp.NT) break;
+    const int b = int(unsigned(nn) / unsigned(T)), t = nn - b * T;
+    float* row = dst + (int64_t(b * pp.n + head) * T + t) * pp.d + dd;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<f32x4*>(row + 4 * h) =
+          *reinterpret_cast<const f32x4*>(&E[(r0 + 8 * u) * EPF + q8 * 8 + 4 * h]);
+  }
+}
+
 template <int MODE, bool TR>
 __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp, const bf16* stg,
                                           const EpiCtx& ec) {
@@ -694,7 +873,7 @@ __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp
         const int cl = 4 * u + (lane >> 4);
         const int c = cw + cl;
         const int head = int(unsigned(c) / unsigned(pp.d)), dd = c - head * pp.d;
-        *reinterpret_cast<bf16x4*>(vt + (int64_t(b * pp.n + head) * pp.d + dd) * pp.Tp + slot) =
+        *reinterpret_cast<bf16x4*>(vt + (int64_t(b * pp.n + head) * pp.dp + dd) * pp.Tp + slot) =
             *reinterpret_cast<const bf16x4*>(&E[cl * EPB + 4 * tq]);
       }
     }
@@ -717,13 +896,15 @@ __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp
         while (t >= T) { t -= T; ++b; }
       }
       if (nn < pp.NT)
-        *reinterpret_cast<bf16x8*>(dst + (int64_t(b * pp.n + head) * T + t) * pp.d + dd) =
+        *reinterpret_cast<bf16x8*>(dst + (int64_t(b * pp.n + head) * T + t) * pp.dp + dd) =
             *reinterpret_cast<const bf16x8*>(&E[(r0 + 8 * u) * EPB + q8 * 8]);
     }
   }
 }
 
-template <int MODE>
+// QKO (Q / K epilogue): 0 the plain bf16 store, 1 the optional query/key
+// steps applied in the epilogue, 2 fp32 Q and K into the qk32 region.
+template <int MODE, int QKO>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(ProjParams pp, int mtiles) {
   __shared__ __attribute__((aligned(16))) bf16 lds0[(GM + GN) * GP];
   __shared__ __attribute__((aligned(16))) bf16 lds1[(GM + GN) * GP];
@@ -761,16 +942,22 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(ProjParams pp, int mt
     gemm_main<MODE, true>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
     epilogue_inputs(pe, ee);
     __syncthreads();  // every wave is done reading the operand tiles
-    if (valid) epi_stage<MODE, true>(acc, ep, pe, stg, ee);
+    if (valid) epi_stage<MODE, true, QKO>(acc, ep, pe, stg, ee);
     __syncthreads();
     if (valid) epi_store<MODE, true>(ep, pe, stg, ee);
   } else {
     gemm_main<MODE, false>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
     epilogue_inputs(pe, ee);
     __syncthreads();
-    if (valid) epi_stage<MODE, false>(acc, ep, pe, stg, ee);
-    __syncthreads();
-    if (valid) epi_store<MODE, false>(ep, pe, stg, ee);
+    if (valid) epi_stage<MODE, false, QKO>(acc, ep, pe, stg, ee);
+    __syncthreads();  // (QKO 1, d = 128: a wave also reads its column partner's region)
+    if constexpr (MODE == kQkv && QKO == 1) {
+      if (valid) epi_store_qkopt(pe, lds0, lds1, ee, wave);
+    } else if constexpr (MODE == kQkv && QKO == 2) {
+      if (valid) epi_store_qk32(pe, stg, ee);
+    } else {
+      if (valid) epi_store<MODE, false>(ep, pe, stg, ee);
+    }
   }
 }
 
@@ -900,25 +1087,45 @@ ProjParams make_params(const Plan& p, const Args& a, int mode) {
   pp.n = int(p.n);
   pp.d = int(p.d);
   pp.Tp = int(p.Tp);
+  pp.dp = int(p.dp);
   pp.M = mode == kQkv ? int(3 * p.C) : int(p.C);
-  pp.q_scale = 1.4426950408889634f / sqrtf(float(p.d));
+  pp.q_scale = kLog2e / sqrtf(float(p.d));
   pp.NT = p.B * p.T;
+  if (mode == kQkv && p.dtype == SSA_BF16) {
+    pp.gq = a.q_norm_gamma;
+    pp.gk = a.k_norm_gamma;
+    pp.rope = a.rope ? 1 : 0;
+    pp.rope_tab = reinterpret_cast<const float2*>(a.ws + p.ws.rope);
+    if (!p.qk_fuse && (a.rope || a.q_norm_gamma != nullptr))
+      pp.qk32 = reinterpret_cast<float*>(a.ws + p.ws.qk32);
+  }
   return pp;
 }
 
 template <int MODE>
 hipError_t launch_mode(const Plan& p, const Args& a) {
   const ProjParams pp = make_params(p, a, MODE);
-  if (p.dtype == SSA_BF16 && p.C % 64 == 0 && p.T % 4 == 0) {
+  const bool main = MODE == kQkv ? p.qkv_main
+                                 : p.dtype == SSA_BF16 && p.C % 64 == 0 && p.T % 4 == 0;
+  if (main) {
     const int mtiles = int((pp.M + GM - 1) / GM);
     const int64_t ntiles = (pp.NT + GN - 1) / GN;
-    gemm_bf16_kernel<MODE><<<dim3(unsigned(mtiles * ntiles)), 256, 0, a.stream>>>(pp, mtiles);
+    const dim3 grid(unsigned(mtiles * ntiles));
+    const bool opt = pp.rope != 0 || pp.gq != nullptr;
+    if (MODE == kQkv && opt && p.qk_fuse)
+      gemm_bf16_kernel<MODE, 1><<<grid, 256, 0, a.stream>>>(pp, mtiles);
+    else if (MODE == kQkv && opt)
+      gemm_bf16_kernel<MODE, 2><<<grid, 256, 0, a.stream>>>(pp, mtiles);
+    else
+      gemm_bf16_kernel<MODE, 0><<<grid, 256, 0, a.stream>>>(pp, mtiles);
   } else if (p.dtype == SSA_BF16) {
     dim3 grid(unsigned((pp.NT + BN - 1) / BN), unsigned((pp.M + BM - 1) / BM));
-    if (MODE == kOut || p.T % 4 != 0)
-      proj_bf16_kernel<MODE, false><<<grid, 256, 0, a.stream>>>(pp);
-    else
-      proj_bf16_kernel<MODE, true><<<grid, 256, 0, a.stream>>>(pp);
+    const bool quad = MODE == kQkv && p.T % 4 == 0;
+    const bool v8 = p.C % 8 == 0;
+    if (quad && v8) proj_bf16_kernel<MODE, true, true><<<grid, 256, 0, a.stream>>>(pp);
+    else if (quad) proj_bf16_kernel<MODE, true, false><<<grid, 256, 0, a.stream>>>(pp);
+    else if (v8) proj_bf16_kernel<MODE, false, true><<<grid, 256, 0, a.stream>>>(pp);
+    else proj_bf16_kernel<MODE, false, false><<<grid, 256, 0, a.stream>>>(pp);
   } else {
     dim3 grid(unsigned((pp.NT + FN - 1) / FN), unsigned((pp.M + FM - 1) / FM));
     proj_f32_kernel<MODE><<<grid, 256, 0, a.stream>>>(pp);

@@ -1,5 +1,4 @@
-// Optional per-head steps between the projections and the scores, in place on
-// the workspace Q and K (B, n, T, d):
+// Optional per-head steps between the projections and the scores:
 //  * query/key normalisation (vit-pytorch simple_vit_with_qk_norm.py, class
 //    RMSNorm): x / max(||x||_2, 1e-12) * sqrt(d) * gamma[head];
 //  * rotary embedding over the token index t (HNDL attention operator,
@@ -9,17 +8,16 @@
 //    the float32 construction the page describes.
 // Normalisation comes first, then the rotation (which keeps norms).
 //
-// General kernel: one group of P lanes (P a power of two >= ceil(d/2)) owns
-// one (token, head) row; lane i holds elements i and i + ceil(d/2).  The
-// squared norm is summed over the group with lane shuffles.
-// bf16 kernel for d % 8 == 0: one group of P lanes owns one (sample, token)
-// and walks the 2n rows of Q and K that share it (every head), lane j holding
-// elements 4j..4j+3 and d/2 + 4j..4j+3 as 8-byte vectors; the rotation's
-// sines and cosines depend only on (token, element), so a lane forms its four
-// once for all 2n rows.  The bf16 queries arrive multiplied by
-// log2(e)/sqrt(d) (the attention kernel's score scale): normalisation removes
-// that factor, so normalised bf16 queries are multiplied by log2(e) (scores in
-// the log2 domain, no 1/sqrt(d)); the rotation is linear and keeps it.
+// Where the QKV projection's epilogue applies both steps itself (bf16, head
+// sizes 16, 32, 64, 128 on its main path), this file only provides the
+// rotation's (cos, sin) table for it.  Otherwise the projection leaves Q and
+// K unrounded -- fp32 in the qk32 region (bf16 problems) or in the fp32 q / k
+// layouts themselves -- and qk_post_kernel applies the steps and writes the q
+// and k layouts, so that bf16 Q and K are rounded once.
+//
+// Also here: zeroing the padding columns d .. dp-1 of bf16 q and k (heads
+// narrower than the attention kernels' operand width), which keeps every
+// score unchanged.
 #include <math.h>
 
 #include "ssa_internal.h"
@@ -28,20 +26,70 @@ namespace ssa {
 namespace {
 
 constexpr int kMaxHalf = 64;  // d <= 128
+constexpr float kLog2e = 1.4426950408889634f;
 
-struct QkPostParams {
-  void* q;             // (B, n, T, d)
-  void* k;
-  const void* gq;      // (n, d) or NULL
-  const void* gk;
-  int T, n, d, hd;     // hd = ceil(d / 2)
-  int rows;            // B * n * T rows in each of Q and K
-  int rope;
-  float qmul;          // extra factor on normalised queries (log2(e) for bf16, 1 for fp32)
+// theta_i = 10000^(-2i/d) rounded to float32 (double on the host, as the
+// angles of the page are built), i < ceil(d/2).
+void fill_theta(float* theta, int64_t d) {
+  const int64_t hd = (d + 1) / 2;
+  for (int64_t i = 0; i < hd && i < kMaxHalf; ++i)
+    theta[i] = float(pow(10000.0, -2.0 * double(i) / double(d)));
+}
+
+struct RopeTabParams {
+  float2* tab;  // (T, d/2): (cos, sin) of t * theta_i
+  int T, hd;
   float theta[kMaxHalf];
 };
 
-template <typename T, int P>
+// grid (ceil(T / 64), d/2): block y is pair i (theta_i read with a uniform
+// index), lane x token t.
+__global__ __launch_bounds__(64) void rope_table_kernel(RopeTabParams rp) {
+  const int i = blockIdx.y;
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t >= rp.T) return;
+  const float ang = float(t) * rp.theta[i];  // one float32 product
+  float s, c;
+  sincosf(ang, &s, &c);
+  rp.tab[int64_t(t) * rp.hd + i] = make_float2(c, s);
+}
+
+struct ZeroPadParams {
+  bf16* q;
+  bf16* k;
+  int64_t rows;  // B * n * T rows in each of q and k
+  int d, dp;
+};
+
+// One thread per (row, padding element) of q, then of k.
+__global__ __launch_bounds__(256) void zero_pad_kernel(ZeroPadParams zp) {
+  const int w = zp.dp - zp.d;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= 2 * zp.rows * w) return;
+  const int64_t r = i / w;
+  const int c = zp.d + int(i - r * w);
+  bf16* base = r < zp.rows ? zp.q + r * zp.dp : zp.k + (r - zp.rows) * zp.dp;
+  base[c] = static_cast<bf16>(0.f);
+}
+
+struct QkPostParams {
+  const float* sq;     // (B, n, T, d) fp32 Q and K as projected (bias added, unscaled)
+  const float* sk;
+  void* q;             // destination layouts (B, n, T, dp)
+  void* k;
+  const void* gq;      // (n, d) or NULL
+  const void* gk;
+  int T, n, d, dp, hd; // hd = ceil(d / 2)
+  int rows;            // B * n * T rows in each of Q and K
+  int rope;
+  float qmul;          // factor on the stored queries (bf16: the score scale in log2 units)
+  float theta[kMaxHalf];
+};
+
+// One group of P lanes (P a power of two >= ceil(d/2)) per (token, head) row;
+// lane i holds elements i and i + ceil(d/2); the squared norm is summed over
+// the group with lane shuffles.  Reads fp32, writes DT once.
+template <typename DT, int P>
 __global__ __launch_bounds__(256) void qk_post_kernel(QkPostParams pp) {
   const int tid = threadIdx.x;
   const int i = tid % P;
@@ -49,19 +97,20 @@ __global__ __launch_bounds__(256) void qk_post_kernel(QkPostParams pp) {
   const bool live = grow < 2 * pp.rows;               // uniform over the P-lane group
   const bool isq = grow < pp.rows;
   const int row = live ? (isq ? grow : grow - pp.rows) : 0;
-  T* base = static_cast<T*>(isq ? pp.q : pp.k) + int64_t(row) * pp.d;
+  const float* src = (isq ? pp.sq : pp.sk) + int64_t(row) * pp.d;
+  DT* dst = static_cast<DT*>(isq ? pp.q : pp.k) + int64_t(row) * pp.dp;
   const int t = row % pp.T;
   const int head = (row / pp.T) % pp.n;
   const int hd = pp.hd, d = pp.d;
   const bool ha = live && i < hd, hb = live && i < hd && i + hd < d;
-  float a = ha ? to_f32(base[i]) : 0.f;
-  float b = hb ? to_f32(base[i + hd]) : 0.f;
-  const T* g = static_cast<const T*>(isq ? pp.gq : pp.gk);
+  float a = ha ? src[i] : 0.f;
+  float b = hb ? src[i + hd] : 0.f;
+  const DT* g = static_cast<const DT*>(isq ? pp.gq : pp.gk);
   if (g != nullptr) {
     float ss = a * a + b * b;
 #pragma unroll
     for (int m = P / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, P);
-    const float f = sqrtf(float(d)) / fmaxf(sqrtf(ss), 1e-12f) * (isq ? pp.qmul : 1.f);
+    const float f = sqrtf(float(d)) / fmaxf(sqrtf(ss), 1e-12f);
     if (ha) a *= f * to_f32(g[head * d + i]);
     if (hb) b *= f * to_f32(g[head * d + i + hd]);
   }
@@ -73,94 +122,24 @@ __global__ __launch_bounds__(256) void qk_post_kernel(QkPostParams pp) {
     a = na;
     b = nb;
   }
-  if (ha) base[i] = from_f32<T>(a);
-  if (hb) base[i + hd] = from_f32<T>(b);
+  const float sc = isq ? pp.qmul : 1.f;
+  if (ha) dst[i] = from_f32<DT>(a * sc);
+  if (hb) dst[i + hd] = from_f32<DT>(b * sc);
 }
 
-template <int P>
-__global__ __launch_bounds__(256) void qk_post_bf16_kernel(QkPostParams pp) {
-  const int tid = threadIdx.x;
-  const int j = tid % P;                          // this lane's element chunk
-  const int item = blockIdx.x * (256 / P) + tid / P;  // (b, t)
-  const int hd = pp.hd, d = pp.d, n = pp.n, T = pp.T;
-  const int nitems = pp.rows / n;                 // B * T
-  if (item >= nitems) return;                     // whole groups leave together
-  const bool act = 4 * j < hd;
-  const int b = item / T, t = item - b * T;
-  const int i = act ? 4 * j : 0;
-  float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-  if (pp.rope) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sincosf(float(t) * pp.theta[i + e], &sn[e], &cs[e]);
-  }
-  const bf16* gq = static_cast<const bf16*>(pp.gq);
-  const bf16* gk = static_cast<const bf16*>(pp.gk);
-  for (int r = 0; r < 2 * n; ++r) {
-    const bool isq = r < n;
-    const int head = isq ? r : r - n;
-    bf16* base = static_cast<bf16*>(isq ? pp.q : pp.k) + ((int64_t(b) * n + head) * T + t) * d;
-    bf16x4 va = {}, vb = {};
-    if (act) {
-      va = *reinterpret_cast<const bf16x4*>(base + i);
-      vb = *reinterpret_cast<const bf16x4*>(base + hd + i);
-    }
-    float a[4], c[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = static_cast<float>(va[e]);
-      c[e] = static_cast<float>(vb[e]);
-    }
-    if (gq != nullptr) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + c[e] * c[e];
-#pragma unroll
-      for (int m = P / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, P);
-      const float f = sqrtf(float(d)) / fmaxf(sqrtf(ss), 1e-12f) * (isq ? pp.qmul : 1.f);
-      if (act) {
-        const bf16* g = (isq ? gq : gk) + head * d;
-        const bf16x4 ga = *reinterpret_cast<const bf16x4*>(g + i);
-        const bf16x4 gb = *reinterpret_cast<const bf16x4*>(g + hd + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] *= f * static_cast<float>(ga[e]);
-          c[e] *= f * static_cast<float>(gb[e]);
-        }
-      }
-    }
-    if (pp.rope) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float na = a[e] * cs[e] - c[e] * sn[e], nc = c[e] * cs[e] + a[e] * sn[e];
-        a[e] = na;
-        c[e] = nc;
-      }
-    }
-    if (act) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        va[e] = static_cast<bf16>(a[e]);
-        vb[e] = static_cast<bf16>(c[e]);
-      }
-      *reinterpret_cast<bf16x4*>(base + i) = va;
-      *reinterpret_cast<bf16x4*>(base + hd + i) = vb;
-    }
-  }
-}
-
-template <typename T>
+template <typename DT>
 hipError_t launch_typed(const QkPostParams& pp, hipStream_t stream) {
   const int hd = pp.hd;
   const int P = hd <= 2 ? 2 : hd <= 4 ? 4 : hd <= 8 ? 8 : hd <= 16 ? 16 : hd <= 32 ? 32 : 64;
   const int64_t rows2 = 2 * int64_t(pp.rows);
   const unsigned grid = unsigned((rows2 * P + 255) / 256);
   switch (P) {
-    case 2: qk_post_kernel<T, 2><<<grid, 256, 0, stream>>>(pp); break;
-    case 4: qk_post_kernel<T, 4><<<grid, 256, 0, stream>>>(pp); break;
-    case 8: qk_post_kernel<T, 8><<<grid, 256, 0, stream>>>(pp); break;
-    case 16: qk_post_kernel<T, 16><<<grid, 256, 0, stream>>>(pp); break;
-    case 32: qk_post_kernel<T, 32><<<grid, 256, 0, stream>>>(pp); break;
-    default: qk_post_kernel<T, 64><<<grid, 256, 0, stream>>>(pp); break;
+    case 2: qk_post_kernel<DT, 2><<<grid, 256, 0, stream>>>(pp); break;
+    case 4: qk_post_kernel<DT, 4><<<grid, 256, 0, stream>>>(pp); break;
+    case 8: qk_post_kernel<DT, 8><<<grid, 256, 0, stream>>>(pp); break;
+    case 16: qk_post_kernel<DT, 16><<<grid, 256, 0, stream>>>(pp); break;
+    case 32: qk_post_kernel<DT, 32><<<grid, 256, 0, stream>>>(pp); break;
+    default: qk_post_kernel<DT, 64><<<grid, 256, 0, stream>>>(pp); break;
   }
   return hipGetLastError();
 }
@@ -169,6 +148,15 @@ hipError_t launch_typed(const QkPostParams& pp, hipStream_t stream) {
 
 hipError_t launch_qk_post(const Plan& p, const Args& a) {
   QkPostParams pp{};
+  const int64_t rows = p.B * p.n * p.T;
+  if (p.dtype == SSA_BF16) {
+    const float* s = reinterpret_cast<const float*>(a.ws + p.ws.qk32);
+    pp.sq = s;
+    pp.sk = s + rows * p.d;
+  } else {  // fp32: in place on the q / k layouts (dp = d)
+    pp.sq = reinterpret_cast<const float*>(a.ws + p.ws.q);
+    pp.sk = reinterpret_cast<const float*>(a.ws + p.ws.k);
+  }
   pp.q = a.ws + p.ws.q;
   pp.k = a.ws + p.ws.k;
   pp.gq = a.q_norm_gamma;
@@ -176,25 +164,40 @@ hipError_t launch_qk_post(const Plan& p, const Args& a) {
   pp.T = int(p.T);
   pp.n = int(p.n);
   pp.d = int(p.d);
+  pp.dp = int(p.dp);
   pp.hd = int((p.d + 1) / 2);
-  pp.rows = int(p.B * p.n * p.T);
+  pp.rows = int(rows);
   pp.rope = a.rope ? 1 : 0;
-  pp.qmul = p.dtype == SSA_BF16 ? 1.4426950408889634f : 1.f;
-  for (int i = 0; i < pp.hd && i < kMaxHalf; ++i)
-    pp.theta[i] = float(pow(10000.0, -2.0 * double(i) / double(p.d)));
-  if (p.dtype == SSA_BF16 && p.d % 8 == 0) {
-    const int chunks = pp.hd / 4;  // 4, 8, 12 or 16
-    const int P = chunks <= 4 ? 4 : chunks <= 8 ? 8 : 16;
-    const int64_t items = p.B * p.T;
-    const unsigned grid = unsigned((items * P + 255) / 256);
-    switch (P) {
-      case 4: qk_post_bf16_kernel<4><<<grid, 256, 0, a.stream>>>(pp); break;
-      case 8: qk_post_bf16_kernel<8><<<grid, 256, 0, a.stream>>>(pp); break;
-      default: qk_post_bf16_kernel<16><<<grid, 256, 0, a.stream>>>(pp); break;
-    }
-    return hipGetLastError();
-  }
+  // bf16 queries carry the score scale (log2 units; no 1/sqrt(d) after the
+  // normalisation); the fp32 attention kernel applies it itself
+  pp.qmul = p.dtype == SSA_BF16
+                ? (a.q_norm_gamma != nullptr ? kLog2e : kLog2e / sqrtf(float(p.d)))
+                : 1.f;
+  fill_theta(pp.theta, p.d);
   return p.dtype == SSA_F32 ? launch_typed<float>(pp, a.stream) : launch_typed<bf16>(pp, a.stream);
+}
+
+hipError_t launch_rope_table(const Plan& p, const Args& a) {
+  RopeTabParams rp{};
+  rp.tab = reinterpret_cast<float2*>(a.ws + p.ws.rope);
+  rp.T = int(p.T);
+  rp.hd = int(p.d / 2);
+  fill_theta(rp.theta, p.d);
+  const dim3 grid(unsigned((p.T + 63) / 64), unsigned(rp.hd));
+  rope_table_kernel<<<grid, 64, 0, a.stream>>>(rp);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_pad(const Plan& p, const Args& a) {
+  ZeroPadParams zp{};
+  zp.q = reinterpret_cast<bf16*>(a.ws + p.ws.q);
+  zp.k = reinterpret_cast<bf16*>(a.ws + p.ws.k);
+  zp.rows = p.B * p.n * p.T;
+  zp.d = int(p.d);
+  zp.dp = int(p.dp);
+  const int64_t total = 2 * zp.rows * (zp.dp - zp.d);
+  zero_pad_kernel<<<dim3(unsigned((total + 255) / 256)), 256, 0, a.stream>>>(zp);
+  return hipGetLastError();
 }
 
 }  // namespace ssa

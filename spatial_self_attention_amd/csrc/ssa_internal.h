@@ -33,6 +33,8 @@ __host__ __device__ __forceinline__ int vt_slot(int t) {
 struct Plan {
   int64_t B, C, H, W, G, n;
   int64_t T, d, Tp;
+  int64_t dp;      // head width of the q, k, vt layouts: d, or for bf16 d rounded up
+                   // to a multiple of 32 (the attention kernels' operand width)
   int dtype;       // ssa_dtype
   int esize;       // bytes per element of x / params / q,k,vt,o
   // GroupNorm statistics split: each (b, g) segment of Cg*T contiguous
@@ -40,6 +42,13 @@ struct Plan {
   int64_t seg_len, chunk, splits;
   int gn_vec;      // elements per vector load in the stats pass (1 = scalar)
   int cus;         // compute units of the current device (launch shaping)
+  // bf16 Q/K/V projection on the 128 x 128 MFMA kernel (C % 64 == 0,
+  // T % 4 == 0, d % 8 == 0); otherwise the general tile kernel
+  bool qkv_main;
+  // query/key normalisation and rotary embedding inside that kernel's
+  // epilogue (qkv_main and d in {16, 32, 64, 128}); otherwise the projection
+  // writes fp32 Q and K to the qk32 region and one pass applies them
+  bool qk_fuse;
   ssa_workspace_layout ws;
 };
 
@@ -60,9 +69,15 @@ struct Args {
   bool rope;
 };
 
-// In-place query/key normalisation and rotary embedding of the workspace Q
-// and K (run inside the QKV stage when either option is on).
+// Query/key normalisation and rotary embedding from the fp32 Q and K that
+// the projection left in the qk32 region, into the bf16 / fp32 q and k
+// layouts (the QKV stage when an option is on and qk_fuse is false).
 hipError_t launch_qk_post(const Plan& p, const Args& a);
+// (cos, sin) of the rotary angles of every (token, pair) into the rope region
+// (the QKV stage when rotary embeddings are on and qk_fuse is true).
+hipError_t launch_rope_table(const Plan& p, const Args& a);
+// Zeros in the padding columns d .. dp-1 of the q and k layouts (bf16, dp > d).
+hipError_t launch_zero_pad(const Plan& p, const Args& a);
 
 // Launchers (one per stage); each returns hipSuccess or the launch error.
 hipError_t launch_gn_stats(const Plan& p, const Args& a);

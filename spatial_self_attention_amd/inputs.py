@@ -9,7 +9,7 @@ block is measured on; the parameter names and shapes are the ten keys of the
 problem statement's parameter table (tensortonic "Spatial Self-Attention",
 parameter table):
 
-* x ~ N(0, x_std) of shape (B, C, H, W)
+* x ~ N(x_mean, x_std) of shape (B, C, H, W) (x_mean 0 for every workload)
 * norm_weight = 1 + N(0, 0.1), norm_bias ~ N(0, 0.1), both (C,)
 * q/k/v/out_weight ~ U(-1/sqrt(C), 1/sqrt(C)), (C, C)   (nn.Linear's range)
 * q/k/v/out_bias ~ N(0, 0.02), (C,)
@@ -55,6 +55,7 @@ class Workload:
     num_groups: int
     num_heads: int
     x_std: float = 1.0
+    x_mean: float = 0.0  # a constant offset of every x value (a DC component)
 
     @property
     def T(self) -> int:
@@ -98,7 +99,7 @@ def draw(wl: Workload, seed: int, stress: bool = False):
     """
     rng = np.random.default_rng(seed)
     B, C, H, W = wl.B, wl.C, wl.H, wl.W
-    x = rng.standard_normal((B, C, H, W)) * wl.x_std
+    x = rng.standard_normal((B, C, H, W)) * wl.x_std + wl.x_mean
     bound = 1.0 / np.sqrt(C)
     raw = {}
     for key in _DRAW_ORDER:

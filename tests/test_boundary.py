@@ -45,11 +45,18 @@ def test_status_strings():
 def _layout_expect(B, C, H, W, G, n, esize):
     T = H * W
     d = C // n
+    dp = d if esize == 4 else -(-d // 32) * 32      # bf16 heads padded to a multiple of 32
     Tp = (T + 63) // 64 * 64
+    fuse = esize == 2 and C % 64 == 0 and T % 4 == 0 and d in (16, 32, 64, 128)
     return {
         "gn_stats": B * G * 8, "gn_coef": B * C * 8,
-        "q": B * n * T * d * esize, "k": B * n * T * d * esize,
-        "vt": B * n * d * Tp * esize, "o": B * T * C * esize,
+        "q": B * n * T * dp * esize, "k": B * n * T * dp * esize,
+        "vt": B * n * dp * Tp * esize, "o": B * T * C * esize,
+        # rotary (cos, sin) table where the projection epilogue runs the
+        # optional steps, else fp32 Q and K for the separate pass (bf16 only)
+        "rope": T * (d // 2) * 8 if fuse else 0,
+        "qk32": 2 * B * T * C * 4 if (esize == 2 and not fuse) else 0,
+        "d_pad": dp,
     }
 
 
@@ -61,6 +68,9 @@ def _layout_expect(B, C, H, W, G, n, esize):
     (2, 640, 96, 96, 32, 10, ssa.SSA_BF16),
     (2, 4, 1, 1, 4, 2, ssa.SSA_F32),
     (1, 2, 2, 3, 1, 1, ssa.SSA_F32),
+    (2, 4, 1, 1, 4, 2, ssa.SSA_BF16),      # d = 2, padded to 32
+    (2, 192, 8, 8, 8, 4, ssa.SSA_BF16),    # d = 48, padded to 64
+    (2, 128, 8, 8, 8, 8, ssa.SSA_BF16),    # d = 16, padded to 32
 ])
 def test_workspace_layout(shape):
     B, C, H, W, G, n, dt = shape
@@ -68,12 +78,13 @@ def test_workspace_layout(shape):
     assert lay["total"] == ssa.ssa_workspace_size(B, C, H, W, G, n, dt)
     esize = 4 if dt == ssa.SSA_F32 else 2
     want = _layout_expect(B, C, H, W, G, n, esize)
+    assert lay["d_pad"] == want.pop("d_pad")
     want["gn_partial"] = B * G * lay["gn_splits"] * 16
-    order = ["gn_partial", "gn_stats", "gn_coef", "q", "k", "vt", "o"]
+    order = ["gn_partial", "gn_stats", "gn_coef", "q", "k", "vt", "o", "rope", "qk32"]
     for a, b in zip(order, order[1:]):
         assert lay[a] % 256 == 0
         assert lay[a] + want[a] <= lay[b], (a, b)
-    assert lay["o"] + want["o"] <= lay["total"]
+    assert lay["qk32"] + want["qk32"] <= lay["total"]
     assert lay["t_pad"] % 64 == 0 and lay["t_pad"] >= H * W
     assert lay["gn_splits"] >= 1
     # every chunk of a segment is non-empty
@@ -83,7 +94,7 @@ def test_workspace_layout(shape):
 
 def test_workspace_size_zero_when_rejected_or_empty():
     assert ssa.ssa_workspace_size(1, 6, 2, 2, 4, 2, ssa.SSA_F32) == 0     # 4 does not divide 6
-    assert ssa.ssa_workspace_size(1, 64, 2, 2, 8, 4, ssa.SSA_BF16) == 0   # d = 16 in bf16
+    assert ssa.ssa_workspace_size(1, 256, 2, 2, 8, 1, ssa.SSA_BF16) == 0  # d = 256
     assert ssa.ssa_workspace_size(0, 64, 8, 8, 8, 2, ssa.SSA_F32) == 0    # empty
     assert ssa.ssa_workspace_size(1, 64, 8, 8, 8, 2, 5) == 0              # dtype
 
@@ -126,8 +137,7 @@ OK_SHAPE = (2, 64, 4, 4, 8, 2, ssa.SSA_BF16)
     ("n does not divide C", dict(shape=(2, 64, 4, 4, 8, 3, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
     ("G = 0", dict(shape=(2, 64, 4, 4, 0, 2, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
     ("n = 0", dict(shape=(2, 64, 4, 4, 8, 0, ssa.SSA_F32)), "SSA_E_CONSTRAINT"),
-    ("bf16 d = 16", dict(shape=(2, 64, 4, 4, 8, 4, ssa.SSA_BF16)), "SSA_E_UNSUPPORTED"),
-    ("bf16 d = 48", dict(shape=(2, 96, 4, 4, 8, 2, ssa.SSA_BF16)), "SSA_E_UNSUPPORTED"),
+    ("bf16 d = 136", dict(shape=(2, 272, 4, 4, 8, 2, ssa.SSA_BF16)), "SSA_E_UNSUPPORTED"),
     ("fp32 d = 256", dict(shape=(2, 256, 4, 4, 8, 1, ssa.SSA_F32)), "SSA_E_UNSUPPORTED"),
     ("too many elements", dict(shape=(1 << 20, 512, 64, 64, 32, 4, ssa.SSA_BF16)),
      "SSA_E_UNSUPPORTED"),

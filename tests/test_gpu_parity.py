@@ -76,6 +76,10 @@ STAGE_CASES = [
     # a large batch of small images: 3120 QKV and 1040 output-projection tiles,
     # several rounds of work-groups on a 256-CU chip
     Workload("many samples", "bf16", 520, 128, 16, 16, 8, 2),
+    # bf16 heads narrower than the attention operand: q, k zero-padded to dp
+    Workload("bf16 d48 padded", "bf16", 2, 192, 6, 10, 8, 4),
+    Workload("bf16 d16 padded", "bf16", 1, 64, 7, 9, 4, 4),
+    Workload("bf16 d2 padded", "bf16", 2, 4, 2, 3, 2, 2),
 ]
 
 
@@ -102,9 +106,15 @@ def test_stage_parity(wl):
 
     tol = 1e-4 if wl.dtype == "f32" else 1e-2
     heads = lambda M: M.reshape(B, T, n, d).transpose(0, 2, 1, 3)     # (B, n, T, d)
-    q, _ = region(ws, wl, "q", edt, (B, n, T, d))
-    k, _ = region(ws, wl, "k", edt, (B, n, T, d))
-    vt, _ = region(ws, wl, "vt", edt, (B, n, d, lay["t_pad"]))
+    dp = lay["d_pad"]
+    assert dp == (d if wl.dtype == "f32" else -(-d // 32) * 32)
+    q, _ = region(ws, wl, "q", edt, (B, n, T, dp))
+    k, _ = region(ws, wl, "k", edt, (B, n, T, dp))
+    # the padding columns of q and k are zero (the workspace was NaN-filled)
+    assert (q[..., d:] == 0).all() and (k[..., d:] == 0).all()
+    q, k = q[..., :d], k[..., :d]
+    vt, _ = region(ws, wl, "vt", edt, (B, n, dp, lay["t_pad"]))
+    vt = vt[:, :, :d]
     if wl.dtype == "bf16":  # bf16 V^T columns hold token t at t with bits 2 and 3 swapped
         t = np.arange(lay["t_pad"])
         vt = vt[..., (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1)]
@@ -174,6 +184,20 @@ EDGE_CASES = [
     Workload("fp32 d=3", "f32", 2, 6, 4, 5, 3, 2),
     Workload("fp32 d=100", "f32", 1, 200, 3, 7, 8, 2),
     Workload("fp32 d=128 T=130", "f32", 1, 256, 10, 13, 8, 2),
+    # the page's worked-example shapes in bf16 (d = 2, 2, 2: heads zero-padded
+    # to 32; C not a multiple of 8, so the general projection kernel)
+    Workload("page ex1 bf16", "bf16", 1, 4, 2, 2, 2, 2),
+    Workload("page ex2 bf16", "bf16", 1, 2, 2, 3, 1, 1),
+    Workload("page ex3 bf16", "bf16", 2, 4, 1, 1, 4, 2),
+    # bf16 head sizes between the attention operand widths (16, 48, 80, 112),
+    # on the 128 x 128 projection kernel (C % 64 == 0) and off it
+    Workload("bf16 d16", "bf16", 2, 128, 9, 12, 8, 8),
+    Workload("bf16 d48", "bf16", 2, 192, 8, 13, 8, 4),
+    Workload("bf16 d80", "bf16", 1, 320, 11, 12, 32, 4),
+    Workload("bf16 d112", "bf16", 1, 448, 10, 10, 32, 4),
+    Workload("bf16 d112 T=61", "bf16", 1, 224, 1, 61, 8, 2),
+    Workload("bf16 d50 C100", "bf16", 2, 100, 6, 6, 4, 2),
+    Workload("bf16 d1 C3", "bf16", 1, 3, 4, 4, 1, 3),
 ]
 
 
@@ -234,6 +258,41 @@ def test_gn_statistics_full_size(idx):
     s_ = p64["norm_bias"][None] - np.repeat(mean, Cg, axis=1) * a
     assert np.max(np.abs(coef[..., 0] - a)) <= 1e-5 * np.max(np.abs(a))
     assert np.max(np.abs(coef[..., 1] - s_)) <= 1e-5 * (1 + np.max(np.abs(a)))
+
+
+# GroupNorm of inputs with a large common offset: x = 50 + N(0, 1), so a
+# group's |mean| is 50 times its standard deviation.  The projection prologue
+# normalises with one FMA, a x + s with s = beta - mean * a, which would lose
+# the deviations if a or s were rounded badly; the statistics pass must also
+# keep the variance (a shifted sum) from cancelling.
+DC_CASES = [
+    Workload("DC offset fp32", "f32", 2, 64, 8, 8, 8, 2, x_mean=50.0),
+    Workload("DC offset fp32 d128", "f32", 1, 256, 12, 12, 32, 2, x_mean=50.0),
+    Workload("DC offset bf16", "bf16", 2, 512, 14, 14, 32, 4, x_mean=50.0),
+    Workload("DC offset bf16 split GN", "bf16", 1, 320, 48, 48, 32, 5, x_mean=50.0),
+]
+
+
+@pytest.mark.parametrize("wl", DC_CASES, ids=lambda w: w.name)
+def test_gn_large_offset(wl):
+    x, p, out, ws = run(wl, 81)
+    x64, p64 = to_f64(x, p)
+    st = ORA.forward_stages(x64, p64, wl.num_groups, wl.num_heads)
+    stats, _ = region(ws, wl, "gn_stats", torch.float32, (wl.B, wl.num_groups, 2))
+    assert np.max(np.abs(stats[..., 0] - st["mean"])) <= 1e-5 * (1 + np.max(np.abs(st["mean"])))
+    assert np.max(np.abs(stats[..., 1] / st["rstd"] - 1)) <= 1e-4
+    e = err(out.double().cpu().numpy(), st["out"], wl.dtype)
+    # the branch out - x alone, against the oracle's (x is ~50 and would hide
+    # an error in the normalised values under the output's own size)
+    gb = out.double().cpu().numpy() - x64
+    wb = st["out"] - x64
+    eb = float(np.max(np.abs(gb - wb)))
+    if wl.dtype == "bf16":
+        eb /= float(np.max(np.abs(wb)))
+    print(f"  err {e:.3e}  branch err {eb:.3e}", flush=True)
+    assert e <= TOL[wl.dtype]
+    if wl.dtype == "f32":
+        assert eb <= 1e-4
 
 
 def test_largest_accepted_call():
