@@ -90,7 +90,8 @@ typedef enum {
                              workspace overlaps an input                        */
   SSA_E_ALIGN = 8,        /* a pointer is not 16-byte aligned                   */
   SSA_E_HIP = 9,          /* a HIP launch failed (e.g. no gfx950 code object)   */
-  SSA_E_STAGE = 10        /* unknown stage code                                 */
+  SSA_E_STAGE = 10,       /* unknown stage code                                 */
+  SSA_E_SCRATCH = 11      /* ssa_forward_noalloc: workspace above its maximum   */
 } ssa_status;
 
 typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
@@ -224,6 +225,31 @@ ssa_status ssa_forward_stage_ex(int stage,
                                 int64_t num_groups, int64_t num_heads, int dtype,
                                 const ssa_options* options,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same block, validation and stream semantics, with the workspace taken from
+ * a static array of the library (ssa_noalloc_max_workspace() bytes, 128 MiB,
+ * on each GPU the library runs on, held until the process ends) instead of a
+ * caller buffer.  It calls no allocating routine.  A problem whose
+ * ssa_workspace_size exceeds the maximum returns SSA_E_SCRATCH before
+ * anything is launched.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * threads) race and may corrupt each other's output; calls ordered on one
+ * stream do not.  The array keeps the last call's intermediates (no kernel
+ * relies on its previous contents). */
+ssa_status ssa_forward_noalloc(const void* x, void* out,
+                               const void* norm_weight, const void* norm_bias,
+                               const void* q_weight, const void* k_weight,
+                               const void* v_weight, const void* out_weight,
+                               const void* q_bias, const void* k_bias,
+                               const void* v_bias, const void* out_bias,
+                               int64_t B, int64_t C, int64_t H, int64_t W,
+                               int64_t num_groups, int64_t num_heads, int dtype,
+                               void* stream);
+
+/* Bytes of the static scratch of ssa_forward_noalloc (its largest workspace). */
+size_t ssa_noalloc_max_workspace(void);
 
 /* 1 when ssa_forward (and ssa_forward_ex with no optional step on) runs the
  * fused stage SSA_STAGE_QKV_ATTENTION for this problem, else 0 (also for

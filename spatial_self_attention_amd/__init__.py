@@ -16,8 +16,9 @@ import torch
 
 from ._binding import (  # noqa: F401
     BIAS_KEYS, EXPORTS, LIB_PATH, PARAM_ORDER, SSA_BF16, SSA_F32, STAGES, Options, SSAError,
-    SSAValueError, lib, ssa_forward, ssa_forward_ex, ssa_forward_stage, ssa_forward_stage_ex,
-    ssa_get_workspace_layout, ssa_status_string, ssa_uses_fused_stage, ssa_workspace_size,
+    SSAValueError, lib, ssa_forward, ssa_forward_ex, ssa_forward_noalloc, ssa_forward_stage,
+    ssa_forward_stage_ex, ssa_get_workspace_layout, ssa_noalloc_max_workspace, ssa_status_string,
+    ssa_uses_fused_stage, ssa_workspace_size,
 )
 from ._binding import _raise
 

@@ -17,6 +17,7 @@ STATUS_NAMES = {
     0: "SSA_OK", 1: "SSA_E_NULL", 2: "SSA_E_SHAPE", 3: "SSA_E_CONSTRAINT",
     4: "SSA_E_DTYPE", 5: "SSA_E_UNSUPPORTED", 6: "SSA_E_WORKSPACE",
     7: "SSA_E_ALIAS", 8: "SSA_E_ALIGN", 9: "SSA_E_HIP", 10: "SSA_E_STAGE",
+    11: "SSA_E_SCRATCH",
 }
 SSA_F32, SSA_BF16 = 0, 1
 STAGES = {"gn_stats": 0, "qkv": 1, "attention": 2, "out_proj": 3, "qkv_attention": 4}
@@ -29,8 +30,8 @@ PARAM_ORDER = (
 )
 
 EXPORTS = ("ssa_workspace_size", "ssa_get_workspace_layout", "ssa_forward",
-           "ssa_forward_ex", "ssa_forward_stage", "ssa_forward_stage_ex", "ssa_uses_fused_stage",
-           "ssa_status_string")
+           "ssa_forward_ex", "ssa_forward_stage", "ssa_forward_stage_ex", "ssa_forward_noalloc",
+           "ssa_noalloc_max_workspace", "ssa_uses_fused_stage", "ssa_status_string")
 
 BIAS_KEYS = ("q_bias", "k_bias", "v_bias", "out_bias")
 
@@ -100,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.ssa_forward_ex.argtypes = fwd[:19] + [ctypes.POINTER(Options)] + fwd[19:]
     L.ssa_forward_stage_ex.restype = ctypes.c_int
     L.ssa_forward_stage_ex.argtypes = [ctypes.c_int] + fwd[:19] + [ctypes.POINTER(Options)] + fwd[19:]
+    L.ssa_forward_noalloc.restype = ctypes.c_int
+    L.ssa_forward_noalloc.argtypes = fwd[:19] + [vp]
+    L.ssa_noalloc_max_workspace.restype = sz
+    L.ssa_noalloc_max_workspace.argtypes = []
     L.ssa_uses_fused_stage.restype = ctypes.c_int
     L.ssa_uses_fused_stage.argtypes = [i64] * 6 + [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -115,7 +120,7 @@ def status_string(status: int) -> str:
 def _raise(status: int, where: str):
     if status == SSA_OK:
         return
-    if status in (1, 2, 3, 4, 5, 6, 7, 8, 10):
+    if status in (1, 2, 3, 4, 5, 6, 7, 8, 10, 11):
         raise SSAValueError(status, where)
     raise SSAError(status, where)
 
@@ -167,6 +172,18 @@ def ssa_forward_stage_ex(stage, x_ptr, out_ptr, param_ptrs, B, C, H, W, num_grou
     return int(lib().ssa_forward_stage_ex(int(stage), x_ptr, out_ptr, *param_ptrs, B, C, H, W,
                                           num_groups, num_heads, int(dtype), opt, ws_ptr,
                                           ws_bytes, stream_ptr))
+
+
+def ssa_forward_noalloc(x_ptr, out_ptr, param_ptrs, B, C, H, W, num_groups, num_heads, dtype,
+                        stream_ptr) -> int:
+    """Raw call of the entry point that allocates nothing (the library's static
+    scratch is the workspace): integer device pointers in, status code out."""
+    return int(lib().ssa_forward_noalloc(x_ptr, out_ptr, *param_ptrs, B, C, H, W, num_groups,
+                                         num_heads, int(dtype), stream_ptr))
+
+
+def ssa_noalloc_max_workspace() -> int:
+    return int(lib().ssa_noalloc_max_workspace())
 
 
 def ssa_uses_fused_stage(B, C, H, W, num_groups, num_heads, dtype) -> bool:

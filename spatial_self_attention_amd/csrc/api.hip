@@ -3,10 +3,20 @@
 // device memory; every check runs before the first launch.
 #include <string.h>
 
+#include <atomic>
+
 #include "ssa_internal.h"
 
 namespace ssa {
 namespace {
+
+// The workspace of ssa_forward_noalloc: a static device array, one per GPU the
+// library runs on, held until the process ends.  128 MiB covers every
+// workload measured here (the high-resolution one needs 97 MB).  In host code
+// `scratch` is only a stand-in symbol: its device address (per device) comes
+// from hipGetSymbolAddress, in scratch_base().
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;  // per tensor, for 32-bit row math
@@ -111,16 +121,25 @@ struct Range {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-ssa_status check_pointers(const Plan& p, const Args& a, size_t ws_bytes) {
+// NULL and alignment checks of the caller's tensors (not the workspace).
+ssa_status check_tensor_pointers(const Args& a) {
   const void* required[] = {a.x, a.out, a.norm_weight, a.norm_bias, a.w[0], a.w[1], a.w[2],
-                            a.w[3], a.ws};
+                            a.w[3]};
   for (const void* q : required)
     if (q == nullptr) return SSA_E_NULL;
   const void* all[] = {a.x, a.out, a.norm_weight, a.norm_bias, a.w[0], a.w[1], a.w[2], a.w[3],
-                       a.b[0], a.b[1], a.b[2], a.b[3], a.ws,
+                       a.b[0], a.b[1], a.b[2], a.b[3],
                        a.rel_pos_table, a.q_norm_gamma, a.k_norm_gamma};
   for (const void* q : all)  // NULL (an absent optional tensor) is aligned
     if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return SSA_E_ALIGN;
+  return SSA_OK;
+}
+
+ssa_status check_pointers(const Plan& p, const Args& a, size_t ws_bytes) {
+  ssa_status st = check_tensor_pointers(a);
+  if (st != SSA_OK) return st;
+  if (a.ws == nullptr) return SSA_E_NULL;
+  if (reinterpret_cast<uintptr_t>(a.ws) % 16 != 0) return SSA_E_ALIGN;
   if (ws_bytes < p.ws.total) return SSA_E_WORKSPACE;
   const size_t e = p.esize;
   const size_t img = size_t(p.B * p.C * p.T) * e;
@@ -152,18 +171,23 @@ ssa_status check_options(const Plan& p, const Args& a) {
   return SSA_OK;
 }
 
+void* scratch_base();
+
 // stages: the stage codes to enqueue, in order; stage < 0: the whole block
 // (stages 0, 1, 2, 3, or 0, 4, 3 where the fused kernel is available and no
-// optional step is on).
+// optional step is on).  workspace NULL with noalloc: the static scratch, once
+// every other argument has been checked.
 ssa_status run(int stage, const void* x, void* out, const void* nw, const void* nb,
                const void* qw, const void* kw, const void* vw, const void* ow,
                const void* qb, const void* kb, const void* vb, const void* ob,
                int64_t B, int64_t C, int64_t H, int64_t W, int64_t G, int64_t n, int dtype,
-               const ssa_options* opt, void* workspace, size_t workspace_bytes, void* stream) {
+               const ssa_options* opt, void* workspace, size_t workspace_bytes, void* stream,
+               bool noalloc = false) {
   Plan p;
   bool empty = false;
   ssa_status st = make_plan(B, C, H, W, G, n, dtype, &p, &empty);
   if (st != SSA_OK || empty) return st;
+  if (noalloc && p.ws.total > kScratchBytes) return SSA_E_SCRATCH;
   Args a;
   a.x = x; a.out = out; a.norm_weight = nw; a.norm_bias = nb;
   a.w[0] = qw; a.w[1] = kw; a.w[2] = vw; a.w[3] = ow;
@@ -176,6 +200,13 @@ ssa_status run(int stage, const void* x, void* out, const void* nw, const void* 
   a.rope = opt != nullptr && opt->rope != 0;
   st = check_options(p, a);
   if (st != SSA_OK) return st;
+  if (noalloc) {
+    st = check_tensor_pointers(a);
+    if (st != SSA_OK) return st;
+    a.ws = static_cast<char*>(scratch_base());
+    if (a.ws == nullptr) return SSA_E_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   st = check_pointers(p, a, workspace_bytes);
   if (st != SSA_OK) return st;
   const bool plain = a.rel_pos_table == nullptr && a.q_norm_gamma == nullptr && !a.rope;
@@ -210,6 +241,20 @@ ssa_status run(int stage, const void* x, void* out, const void* nw, const void* 
     if (e != hipSuccess) return SSA_E_HIP;
   }
   return SSA_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL on a HIP error.
+void* scratch_base() {
+  static std::atomic<void*> base[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = base[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    base[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 }  // namespace
@@ -287,6 +332,19 @@ ssa_status ssa_forward_stage_ex(int stage, const void* x, void* out, const void*
                   num_heads, dtype, options, workspace, workspace_bytes, stream);
 }
 
+ssa_status ssa_forward_noalloc(const void* x, void* out, const void* norm_weight,
+                               const void* norm_bias, const void* q_weight, const void* k_weight,
+                               const void* v_weight, const void* out_weight, const void* q_bias,
+                               const void* k_bias, const void* v_bias, const void* out_bias,
+                               int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
+                               int64_t num_heads, int dtype, void* stream) {
+  return ssa::run(-1, x, out, norm_weight, norm_bias, q_weight, k_weight, v_weight, out_weight,
+                  q_bias, k_bias, v_bias, out_bias, B, C, H, W, num_groups, num_heads, dtype,
+                  nullptr, nullptr, 0, stream, /*noalloc=*/true);
+}
+
+size_t ssa_noalloc_max_workspace(void) { return ssa::kScratchBytes; }
+
 int ssa_uses_fused_stage(int64_t B, int64_t C, int64_t H, int64_t W, int64_t num_groups,
                          int64_t num_heads, int dtype) {
   ssa::Plan p;
@@ -313,6 +371,9 @@ const char* ssa_status_string(int status) {
     case SSA_E_ALIGN: return "a pointer is not 16-byte aligned";
     case SSA_E_HIP: return "a HIP kernel launch failed";
     case SSA_E_STAGE: return "unknown stage";
+    case SSA_E_SCRATCH:
+      return "ssa_forward_noalloc: the problem's workspace exceeds the library's static scratch "
+             "(ssa_noalloc_max_workspace() bytes); use ssa_forward with a caller workspace";
     default: return "unknown status";
   }
 }

@@ -279,3 +279,42 @@ def test_ex_valid_options_reach_the_workspace_check():
     opt = bnd.Options(1 << 50, 1 << 51, (1 << 51) + (1 << 30), 1)
     assert call_ex(OK_SHAPE, opt, ws_bytes=1024) == "SSA_E_WORKSPACE"
     assert call_ex(OK_SHAPE, None, ws_bytes=1024) == "SSA_E_WORKSPACE"
+
+
+# ---------------------------------------------------------------------------
+# ssa_forward_noalloc: host-side checks (no device call is made on these paths)
+# ---------------------------------------------------------------------------
+
+def call_noalloc(shape, ptr=None):
+    B, C, H, W, G, n, dt = shape
+    fake = Fake()
+    p = {k: fake() for k in ["x", "out"] + list(bnd.PARAM_ORDER)}
+    p.update(ptr or {})
+    st = ssa.ssa_forward_noalloc(p["x"], p["out"], [p[k] for k in bnd.PARAM_ORDER],
+                                 B, C, H, W, G, n, dt, 0)
+    return bnd.STATUS_NAMES[st]
+
+
+def test_noalloc_limit_covers_the_workloads():
+    from spatial_self_attention_amd.inputs import WORKLOADS
+    lim = ssa.ssa_noalloc_max_workspace()
+    assert lim == 128 << 20
+    for wl in WORKLOADS:
+        need = ssa.ssa_workspace_size(wl.B, wl.C, wl.H, wl.W, wl.num_groups, wl.num_heads,
+                                      ssa.dtype_code(wl.torch_dtype))
+        assert 0 < need <= lim, wl.name
+
+
+def test_noalloc_rejects_above_its_scratch():
+    # 64 x 512 x 64 x 64 bf16: about 1 GB of workspace
+    shape = (64, 512, 64, 64, 32, 8, ssa.SSA_BF16)
+    assert ssa.ssa_workspace_size(*shape) > ssa.ssa_noalloc_max_workspace()
+    assert call_noalloc(shape) == "SSA_E_SCRATCH"
+
+
+def test_noalloc_validates_before_touching_the_device():
+    assert call_noalloc(OK_SHAPE, ptr={"x": 0}) == "SSA_E_NULL"
+    assert call_noalloc(OK_SHAPE, ptr={"q_weight": (1 << 44) + 8}) == "SSA_E_ALIGN"
+    assert call_noalloc((2, 6, 4, 4, 4, 2, ssa.SSA_BF16)) == "SSA_E_CONSTRAINT"
+    assert call_noalloc((2, 64, 4, 4, 8, 2, 7)) == "SSA_E_DTYPE"
+    assert call_noalloc((0, 64, 4, 4, 8, 2, ssa.SSA_BF16)) == "SSA_OK"   # empty: nothing to do
