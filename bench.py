@@ -94,7 +94,7 @@ def stage_work(wl):
 STAGE_KERNELS = {
     "gn_stats": "gn_stats_kernel (+ gn_finalize_kernel when segments are split)",
     "qkv": "gemm_bf16_kernel<0, *>",
-    "attention": "attn_bf16_kernel / attn2_bf16_kernel / attn2s_bf16_kernel",
+    "attention": "attn_bf16_kernel / attn2_bf16_kernel / attnpp_bf16_kernel",
     "qkv_attention": "fused_bf16_kernel",
     "out_proj": "gemm_bf16_kernel<1, 0>",
 }

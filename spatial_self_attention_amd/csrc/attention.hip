@@ -684,26 +684,55 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
                 lds + wave * 64 * (D + 8));
 }
 
-// 256-query tiles, one per CU: 8 waves, the two halves of the work-group
-// (waves 0-3 and 4-7) taking the same 256 queries against the two halves of
-// the key tiles, each half with its own tile stream (two waves per SIMD, as
-// with two 4-wave work-groups, but a CU finishes one tile at a time).  Half 1
-// leaves (O, m, l) in LDS and half 0 merges:
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel: two wave groups in alternation (d = 64, long sequences)
+// ---------------------------------------------------------------------------
+// One 256-query tile per work-group of 8 waves; waves 0-3 (group 0) and 4-7
+// (group 1) take the same 256 queries (64 per wave, two 32-query blocks)
+// against the two halves of the keys, so a CU finishes one tile at a time and
+// a partial last round of tiles is a round of whole CUs.  Group 1 leaves its
+// (O, m, l) in LDS at the end and group 0 merges:
 //   O = O_0 2^(m_0 - M) + O_1 2^(m_1 - M),  l likewise,  M = max(m_0, m_1).
-// Needs an even number of key tiles, all full.
+// A SIMD holds one wave of each group (waves s and s + 4).  Each wave
+// alternates two kinds of half step over its 32-key sub-blocks j:
+//   M_j  the MFMAs: scores S_j = K_j Q^T - m of both query blocks (8), then
+//        O^T += V_{j-1}^T P_{j-1}^T of both (8);
+//   V_j  the softmax of S_j on the VALU (bf16 probabilities P_j, row sums,
+//        the lazy raise of m) and the LDS reads of the operand fragments the
+//        next M needs (K_{j+1}, V_j).
+// The groups run half a step apart and every half step ends at a barrier of
+// all 8 waves, so on each SIMD one wave's MFMAs run while the other wave's
+// softmax runs: the matrix core and the VALU work side by side instead of
+// both waves of a SIMD wanting the same unit at the same time (which is what
+// a tile barrier shared by two waves in step produces).  The barriers carry no
+// memory fence: each wave waits for its own tile loads explicitly.
+// Key tiles (64 keys: two sub-blocks) go from global memory straight into LDS,
+// three buffers per group: tile u+2 is requested in M_{2u+1} (its buffer held
+// tile u-1, last read in V_{2u-1}) and waited for at the end of V_{2u+2}, the
+// half step before its first read (V_{2u+3} reads K_{2u+4}) -- at that point
+// no later load of the wave is outstanding, so every wait is vmcnt(0).
+// Needs T % 128 == 0 (whole tiles, an even number of them).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, int KT>
-__global__ __launch_bounds__(512, 1) void attn2s_bf16_kernel(AttnParams ap) {
-  typedef Tile<D, 2, KT, 4> TL;  // one half's geometry
-  constexpr int kState = 4 * 64 * (2 * (D / 32) * 16 + 4);  // floats: half 1's O, m, l
-  constexpr int kMerge = kState * 2 + 4 * 64 * (D + 8);     // + half 0's output staging (bf16)
-  // 2 halves x 2 tile buffers; after the tiles, the merge
-  __shared__ __attribute__((aligned(16))) bf16 lds[4 * TL::BUF > kMerge ? 4 * TL::BUF : kMerge];
+__global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
+  typedef Tile<D, 2, KT, 4> TL;  // one group's geometry
+  constexpr int NBUF = 3;
+  static_assert(TL::NKB == 2, "the tile loads are scheduled by sub-block parity");
+  constexpr int kState = 4 * 64 * (2 * (D / 32) * 16 + 4);  // floats: group 1's O, m, l
+  constexpr int kMerge = kState * 2 + 4 * 64 * (D + 8);     // + group 0's output staging (bf16)
+  constexpr int kTiles = 2 * NBUF * TL::BUF;
+  __shared__ __attribute__((aligned(16))) bf16 lds[kTiles > kMerge ? kTiles : kMerge];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int hk = __builtin_amdgcn_readfirstlane(wave >> 2);  // key half
-  const int gw = __builtin_amdgcn_readfirstlane(wave & 3);   // wave within the half
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // key half
+  const int gw = __builtin_amdgcn_readfirstlane(wave & 3);    // wave within the group
   const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   const int qtile = lid % ap.qtiles;
   const int bh = lid / ap.qtiles;
@@ -716,41 +745,83 @@ __global__ __launch_bounds__(512, 1) void attn2s_bf16_kernel(AttnParams ap) {
 
   AttnState<D, 2> st;
   init_state<D, 2>(st, Q, qbase, T, half, col);
-  const int nh = T / KT / 2;  // key tiles per half
-  const int t0 = hk * nh;
-  bf16* mine = lds + hk * 2 * TL::BUF;
-  dma_tile<D, 2, KT, 4>(mine, K, Vt, ap.Tp, t0 * KT, T, gw, lane);
-  Pipe<D> pp;
-  {
-    const bf16x8 z = {};
-    pp.pb1[0] = pp.pb1[1] = z;
-#pragma unroll
-    for (int gp = 0; gp < 2; ++gp)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) pp.vf.a[gp][db] = z;
-  }
-  __syncthreads();
-  read_k<D, 2, KT>(pp.kf, mine, 0, half, col);
-  qk_qb<D>(pp.s0, st, 0, pp.kf);
-  for (int j = 0; j < nh; ++j) {
-    bf16* cur = mine + (j & 1) * TL::BUF;
-    bf16* nxt = mine + ((j + 1) & 1) * TL::BUF;
-    if (j + 1 < nh) dma_tile<D, 2, KT, 4>(nxt, K, Vt, ap.Tp, (t0 + j + 1) * KT, T, gw, lane);
-    pipe_tile<D, KT>(st, pp, cur, (t0 + j) * KT, T, half, col, j == 0);
-    __syncthreads();  // both halves: tile j+1 is in place, tile j is free
-    if (j + 1 < nh) {
-      read_k<D, 2, KT>(pp.kf, nxt, 0, half, col);
-      qk_qb<D>(pp.s0, st, 0, pp.kf);
-    }
-  }
-  pv_qb<D, 2>(st, 1, pp.pb1, pp.vf);
+  const int nh = T / KT / 2;  // key tiles per group
+  const int J = 2 * nh;       // sub-blocks per group
+  const int k0 = grp * nh * KT;
+  bf16* mine = lds + grp * NBUF * TL::BUF;
+  dma_tile<D, 2, KT, 4>(mine, K, Vt, ap.Tp, k0, T, gw, lane);
+  if (nh > 1) dma_tile<D, 2, KT, 4>(mine + TL::BUF, K, Vt, ap.Tp, k0 + KT, T, gw, lane);
+  __syncthreads();  // tiles 0 and 1 of both groups are in place
 
-  // half 1's accumulators, running max and row sums through LDS (register
-  // order: every store and load one row of 64 lanes)
+  KFrag<D> kf;
+  VFrag<D> vf;
+  f32x16 s[2];
+  bf16x8 pb[2][2];
+  // M half step on sub-block kb of the tile in `cur`: K_j's fragments are
+  // read first (their LDS latency hides behind the P V products, and they are
+  // not live during the softmax), then O^T += V_{j-1}^T P_{j-1}^T, then
+  // S_j = K_j Q^T - m.
+  auto m_step = [&](const bf16* cur, int kb, bool pv, bool qk) {
+    if (qk) read_k<D, 2, KT>(kf, cur, kb, half, col);
+    if (pv) {
+      pv_qb<D, 2>(st, 0, pb[0], vf);
+      pv_qb<D, 2>(st, 1, pb[1], vf);
+    }
+    if (qk) {
+      qk_qb<D>(s[0], st, 0, kf);
+      qk_qb<D>(s[1], st, 1, kf);
+    }
+  };
+  // V half step: softmax of S_j; V_j's fragments are read between the two
+  // blocks' softmaxes (needed first by the next M's P V products).
+  auto v_step = [&](const bf16* cur, int kb, bool first) {
+    softmax_qb<D, 2, false>(st, 0, s[0], pb[0], 0, T, half, first);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v<D, 2, KT>(vf, cur + TL::KSZ, kb, half, col);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_qb<D, 2, false>(st, 1, s[1], pb[1], 0, T, half, first);
+  };
+  auto request = [&](int u) {  // tile u of the group into buffer u % 3
+    dma_tile<D, 2, KT, 4>(mine + (u % NBUF) * TL::BUF, K, Vt, ap.Tp, k0 + u * KT, T, gw, lane);
+  };
+
+  if (grp == 1) phase_barrier();  // group 1 runs half a step behind
+  // tile 0: its first sub-block starts the running max
+  m_step(mine, 0, false, true);
+  phase_barrier();
+  v_step(mine, 0, true);
+  phase_barrier();  // (tile 1 arrived before the first barrier)
+  m_step(mine, 1, true, true);
+  if (2 < nh) request(2);
+  phase_barrier();
+  v_step(mine, 1, false);
+  phase_barrier();
+  int bu = 1;  // buffer of tile u
+  for (int u = 1; u < nh; ++u) {
+    const bf16* cur = mine + bu * TL::BUF;
+    m_step(cur, 0, true, true);
+    phase_barrier();
+    v_step(cur, 0, false);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile u + 1 is in
+    phase_barrier();
+    m_step(cur, 1, true, true);
+    if (u + 2 < nh) request(u + 2);    // into the buffer of tile u - 1
+    phase_barrier();
+    v_step(cur, 1, false);
+    phase_barrier();
+    bu = bu + 1 == NBUF ? 0 : bu + 1;
+  }
+  m_step(mine, 0, true, false);  // the last sub-block's P V
+  phase_barrier();
+  if (grp == 0) phase_barrier();  // both groups pass the same number of barriers
+
+  // group 1's accumulators, running max and row sums through LDS (register
+  // order: every store and load one row of 64 lanes), merged by group 0
+  __syncthreads();  // every wave is done with the key tiles
   float* stt = reinterpret_cast<float*>(lds);
   constexpr int kO = 2 * (D / 32) * 16;
   float* my = stt + gw * 64 * (kO + 4);
-  if (hk == 1) {
+  if (grp == 1) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -762,7 +833,7 @@ __global__ __launch_bounds__(512, 1) void attn2s_bf16_kernel(AttnParams ap) {
     }
   }
   __syncthreads();
-  if (hk == 0) {
+  if (grp == 0) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float m1 = my[(kO + qb) * 64 + lane], l1 = my[(kO + 2 + qb) * 64 + lane];
@@ -776,7 +847,6 @@ __global__ __launch_bounds__(512, 1) void attn2s_bf16_kernel(AttnParams ap) {
           st.o[qb][db][r] =
               st.o[qb][db][r] * w0 + my[((qb * (D / 32) + db) * 16 + r) * 64 + lane] * w1;
     }
-    // staging after half 1's state (it is still being read by the other waves)
     write_o<D, 2>(st, ap, b, head, qbase, half, col, lane,
                   reinterpret_cast<bf16*>(stt + kState) + gw * 64 * (D + 8));
   }
@@ -925,13 +995,14 @@ void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream
     }
     if (t256 >= 2 * int64_t(p.cus)) {
       // 256-query tiles.  With an even number of full key tiles each tile runs
-      // as one 8-wave work-group whose halves split the keys: faster per tile
-      // than two 4-wave work-groups sharing a CU, and a partial last round is
-      // then a round of whole CUs; otherwise two 4-wave work-groups per CU.
+      // as one 8-wave work-group whose halves split the keys (attnpp): faster
+      // per tile than two 4-wave work-groups sharing a CU, and a partial last
+      // round is then a round of whole CUs; otherwise two 4-wave work-groups
+      // per CU.
       if (p.T % 128 == 0) {
         typedef Tile<64, 2, 64, 4> TL;
         ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
-        attn2s_bf16_kernel<64, 64><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
+        attnpp_bf16_kernel<64, 64><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
         return;
       }
       launch_bf16_2<64, 64, 4, 2>(ap, bh, stream);
