@@ -712,21 +712,32 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
 // half step before its first read (V_{2u+3} reads K_{2u+4}) -- at that point
 // no later load of the wave is outstanding, so every wait is vmcnt(0).
 // Needs T % 128 == 0 (whole tiles, an even number of them).
+// REL = 2: the 2-D relative-position logit bias, with table slices per key
+// tile in LDS as in attn_bf16_kernel (the slice a key tile needs for the
+// work-group's 256 queries, fp32 times log2(e), and each key's grid term):
+// loaded into registers in the half step that requests the tile, stored to
+// LDS in the next M half step (three slots per group, like the tiles), and
+// added to the scores at the start of each V half step (gathered there: an
+// MFMA half step that waits on LDS holds both waves of its SIMD at the next
+// barrier).
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int KT>
+template <int D, int KT, int REL>
 __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   typedef Tile<D, 2, KT, 4> TL;  // one group's geometry
   constexpr int NBUF = 3;
   static_assert(TL::NKB == 2, "the tile loads are scheduled by sub-block parity");
+  static_assert(REL == 0 || REL == 2, "table slices in LDS only");
   constexpr int kState = 4 * 64 * (2 * (D / 32) * 16 + 4);  // floats: group 1's O, m, l
   constexpr int kMerge = kState * 2 + 4 * 64 * (D + 8);     // + group 0's output staging (bf16)
   constexpr int kTiles = 2 * NBUF * TL::BUF;
   __shared__ __attribute__((aligned(16))) bf16 lds[kTiles > kMerge ? kTiles : kMerge];
+  __shared__ float rel_lds[REL ? 2 * NBUF * kRelSlice : 1];                       // slices
+  __shared__ __attribute__((aligned(16))) int kterm_lds[REL ? 2 * NBUF * KT : 1];  // key terms
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -746,22 +757,87 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   AttnState<D, 2> st;
   init_state<D, 2>(st, Q, qbase, T, half, col);
   const int nh = T / KT / 2;  // key tiles per group
-  const int J = 2 * nh;       // sub-blocks per group
   const int k0 = grp * nh * KT;
   bf16* mine = lds + grp * NBUF * TL::BUF;
+
+  // relative-position bias (REL = 2): the table column of the head, the
+  // work-group's query range, this lane's query terms
+  f32x16 s[2];  // scores of the current sub-block, both query blocks
+  RelPos<2> rp;
+  float rel_pf[REL ? kRelSlice / 256 : 1];  // slice entries of one tile (4 per thread)
+  int kterm_pf = 0;
+  int qrow0[2] = {0, 0};
+  const int gtid = gw * 64 + lane;  // thread within the group
+  const int rq0 = qtile * TL::QT, rq1 = min(rq0 + TL::QT, T) - 1;
+  if constexpr (REL != 0) {
+    rp.tab = static_cast<const bf16*>(ap.rel) + head;
+    rp.H = ap.H;
+    rp.W = ap.W;
+    rp.n = ap.n;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {  // rows past T take the last query's place
+      const int qi = min(qbase + qb * 32 + col, T - 1);
+      const int r = qi / ap.W;
+      qrow0[qb] = (r + ap.H - 1) * (2 * ap.W - 1) + (qi - r * ap.W) + ap.W - 1;
+    }
+  }
+  auto rel_load = [&](int u) {  // slice and key terms of tile u into registers
+    if constexpr (REL != 0) {
+      const int kt = k0 + u * KT;
+      int lo, len;
+      rel_rows(rq0, rq1, kt, kt + KT - 1, ap.H, ap.W, lo, len);
+#pragma unroll
+      for (int e = 0; e < kRelSlice / 256; ++e) {
+        const int i = gtid + 256 * e;
+        rel_pf[e] = i < len ? kLog2e * static_cast<float>(rp.tab[int64_t(lo + i) * ap.n]) : 0.f;
+      }
+      const int key = kt + (gtid & (KT - 1));
+      const int kr = key / ap.W;
+      kterm_pf = kr * (2 * ap.W - 1) + (key - kr * ap.W);
+    }
+  };
+  auto rel_store = [&](int u) {  // into slot u % 3 of the group
+    if constexpr (REL != 0) {
+      const int slot = u % NBUF;
+      float* sl = rel_lds + (grp * NBUF + slot) * kRelSlice;
+#pragma unroll
+      for (int e = 0; e < kRelSlice / 256; ++e) sl[gtid + 256 * e] = rel_pf[e];
+      if (gtid < KT) kterm_lds[(grp * NBUF + slot) * KT + gtid] = kterm_pf;
+    }
+  };
+  auto rel_add = [&](int u, int kb) {  // bias of tile u, sub-block kb, onto the scores
+    if constexpr (REL != 0) {
+      const int kt = k0 + u * KT;
+      int len;
+      rel_rows(rq0, rq1, kt, kt + KT - 1, ap.H, ap.W, rp.lo, len);
+      const int slot = u % NBUF;
+      rp.slice = rel_lds + (grp * NBUF + slot) * kRelSlice;
+      rp.kterm = kterm_lds + (grp * NBUF + slot) * KT;
+      rp.k0 = kt;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) rp.qrow[qb] = qrow0[qb] - rp.lo;
+      add_rel<2, 2>(s, rp, kt + kb * 32, T, half);
+    }
+  };
+
   dma_tile<D, 2, KT, 4>(mine, K, Vt, ap.Tp, k0, T, gw, lane);
   if (nh > 1) dma_tile<D, 2, KT, 4>(mine + TL::BUF, K, Vt, ap.Tp, k0 + KT, T, gw, lane);
-  __syncthreads();  // tiles 0 and 1 of both groups are in place
+  rel_load(0);
+  rel_store(0);
+  if (nh > 1) {
+    rel_load(1);
+    rel_store(1);
+  }
+  __syncthreads();  // tiles 0 and 1 of both groups (and their slices) are in place
 
   KFrag<D> kf;
   VFrag<D> vf;
-  f32x16 s[2];
   bf16x8 pb[2][2];
   // M half step on sub-block kb of the tile in `cur`: K_j's fragments are
   // read first (their LDS latency hides behind the P V products, and they are
   // not live during the softmax), then O^T += V_{j-1}^T P_{j-1}^T, then
   // S_j = K_j Q^T - m.
-  auto m_step = [&](const bf16* cur, int kb, bool pv, bool qk) {
+  auto m_step = [&](const bf16* cur, int u, int kb, bool pv, bool qk) {
     if (qk) read_k<D, 2, KT>(kf, cur, kb, half, col);
     if (pv) {
       pv_qb<D, 2>(st, 0, pb[0], vf);
@@ -774,44 +850,47 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   };
   // V half step: softmax of S_j; V_j's fragments are read between the two
   // blocks' softmaxes (needed first by the next M's P V products).
-  auto v_step = [&](const bf16* cur, int kb, bool first) {
+  auto v_step = [&](const bf16* cur, int u, int kb, bool first) {
+    rel_add(u, kb);
     softmax_qb<D, 2, false>(st, 0, s[0], pb[0], 0, T, half, first);
     __builtin_amdgcn_sched_barrier(0);
     read_v<D, 2, KT>(vf, cur + TL::KSZ, kb, half, col);
     __builtin_amdgcn_sched_barrier(0);
     softmax_qb<D, 2, false>(st, 1, s[1], pb[1], 0, T, half, first);
   };
-  auto request = [&](int u) {  // tile u of the group into buffer u % 3
+  auto request = [&](int u) {  // tile u of the group into buffer u % 3 (slice first)
+    rel_load(u);
     dma_tile<D, 2, KT, 4>(mine + (u % NBUF) * TL::BUF, K, Vt, ap.Tp, k0 + u * KT, T, gw, lane);
   };
 
   if (grp == 1) phase_barrier();  // group 1 runs half a step behind
   // tile 0: its first sub-block starts the running max
-  m_step(mine, 0, false, true);
+  m_step(mine, 0, 0, false, true);
   phase_barrier();
-  v_step(mine, 0, true);
+  v_step(mine, 0, 0, true);
   phase_barrier();  // (tile 1 arrived before the first barrier)
-  m_step(mine, 1, true, true);
+  m_step(mine, 0, 1, true, true);
   if (2 < nh) request(2);
   phase_barrier();
-  v_step(mine, 1, false);
+  v_step(mine, 0, 1, false);
   phase_barrier();
   int bu = 1;  // buffer of tile u
   for (int u = 1; u < nh; ++u) {
     const bf16* cur = mine + bu * TL::BUF;
-    m_step(cur, 0, true, true);
+    m_step(cur, u, 0, true, true);
+    if (u + 1 < nh) rel_store(u + 1);  // requested in the M half step before
     phase_barrier();
-    v_step(cur, 0, false);
+    v_step(cur, u, 0, false);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile u + 1 is in
     phase_barrier();
-    m_step(cur, 1, true, true);
+    m_step(cur, u, 1, true, true);
     if (u + 2 < nh) request(u + 2);    // into the buffer of tile u - 1
     phase_barrier();
-    v_step(cur, 1, false);
+    v_step(cur, u, 1, false);
     phase_barrier();
     bu = bu + 1 == NBUF ? 0 : bu + 1;
   }
-  m_step(mine, 0, true, false);  // the last sub-block's P V
+  m_step(mine, 0, 0, true, false);  // the last sub-block's P V
   phase_barrier();
   if (grp == 0) phase_barrier();  // both groups pass the same number of barriers
 
@@ -958,17 +1037,16 @@ void launch_bf16_2(AttnParams ap, int64_t bh, hipStream_t stream) {
 }
 
 
-// The relative-position variant comes in the 4-wave shape only.  Its table
-// slices go through LDS when every (query tile, key tile) pair's slice fits
-// kRelSlice entries: a query tile spans at most ceil((QT-1)/W) + 1 grid rows
-// and a key tile ceil((KT-1)/W) + 1, and a slice covers (row spans - 1 + 1)
-// blocks of 2W - 1 rows.
+// The relative-position variant of this kernel comes in the 4-wave shape
+// only; its table slices go through LDS when they fit (rel_slice_fits), else
+// each entry is gathered from the table in global memory.
+bool rel_slice_fits(int QT, int KT, int W);
+
 template <int D, int QB, int KT, int NW>
 void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
   if (ap.rel != nullptr) {
     typedef Tile<D, QB, KT, 4> TL;
-    const int64_t spans = (TL::QT - 1 + ap.W - 1) / ap.W + (KT - 1 + ap.W - 1) / ap.W + 1;
-    if (spans * (2 * int64_t(ap.W) - 1) <= kRelSlice)
+    if (rel_slice_fits(TL::QT, KT, ap.W))
       launch_bf16_v<D, QB, KT, 4, 2>(ap, bh, stream);
     else
       launch_bf16_v<D, QB, KT, 4, 1>(ap, bh, stream);
@@ -986,27 +1064,44 @@ void launch_bf16(AttnParams ap, int64_t bh, hipStream_t stream) {
 // when they fill at least one round of two per CU;
 // otherwise (shorter or fewer sequences) the one-block kernel, whose
 // 128-query work-groups spread the work more evenly.
+// True when every (query tile, key tile) pair's slice of the relative-position
+// table fits kRelSlice entries: a query tile of QT spans at most
+// ceil((QT-1)/W) + 1 grid rows and a key tile ceil((KT-1)/W) + 1, and a slice
+// covers (the two spans - 1) blocks of 2W - 1 rows.
+bool rel_slice_fits(int QT, int KT, int W) {
+  const int64_t spans = (QT - 1 + W - 1) / W + (KT - 1 + W - 1) / W + 1;
+  return spans * (2 * int64_t(W) - 1) <= kRelSlice;
+}
+
 void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream) {
-  if (ap.rel == nullptr && p.T >= 1024) {
+  if (p.T >= 1024) {
     const int64_t t512 = bh * ((p.T + 511) / 512), t256 = bh * ((p.T + 255) / 256);
-    if (t512 % p.cus == 0 || t512 >= 4 * int64_t(p.cus)) {
+    if (ap.rel == nullptr && (t512 % p.cus == 0 || t512 >= 4 * int64_t(p.cus))) {
       launch_bf16_2<64, 128, 8, 1>(ap, bh, stream);
       return;
     }
-    if (t256 >= 2 * int64_t(p.cus)) {
+    // (the one-block kernel's relative-position variant runs two work-groups
+    // per CU, so a single round of 256-query tiles already pays for it)
+    if (t256 >= (ap.rel != nullptr ? 1 : 2) * int64_t(p.cus)) {
       // 256-query tiles.  With an even number of full key tiles each tile runs
       // as one 8-wave work-group whose halves split the keys (attnpp): faster
       // per tile than two 4-wave work-groups sharing a CU, and a partial last
       // round is then a round of whole CUs; otherwise two 4-wave work-groups
-      // per CU.
-      if (p.T % 128 == 0) {
+      // per CU.  The relative-position bias takes the same kernel where its
+      // table slices fit.
+      if (p.T % 128 == 0 && (ap.rel == nullptr || rel_slice_fits(256, 64, ap.W))) {
         typedef Tile<64, 2, 64, 4> TL;
         ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
-        attnpp_bf16_kernel<64, 64><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
+        if (ap.rel != nullptr)
+          attnpp_bf16_kernel<64, 64, 2><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
+        else
+          attnpp_bf16_kernel<64, 64, 0><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
         return;
       }
-      launch_bf16_2<64, 64, 4, 2>(ap, bh, stream);
-      return;
+      if (ap.rel == nullptr) {
+        launch_bf16_2<64, 64, 4, 2>(ap, bh, stream);
+        return;
+      }
     }
   }
   launch_bf16<64, 1, 64, 4>(ap, bh, stream);

@@ -171,8 +171,9 @@ def test_relpos_wide_image(flags, stress):
 # plain and stressed draws.
 @pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
 @pytest.mark.parametrize("idx,rel,rope,qkn", [(1, True, True, True), (3, True, True, True),
-                                              (4, False, True, True), (4, False, True, False)],
-                         ids=["1-all", "3-all", "4-qknorm-rope", "4-rope"])
+                                              (4, False, True, True), (4, False, True, False),
+                                              (4, True, False, False), (4, True, True, True)],
+                         ids=["1-all", "3-all", "4-qknorm-rope", "4-rope", "4-relpos", "4-all"])
 def test_options_full_size_sampled(idx, rel, rope, qkn, stress):
     wl = WORKLOADS[idx]
     x, p, opts, out = run_case(wl, 1000 + idx, stress, drop_bias=("k_bias",),
@@ -260,3 +261,27 @@ def test_qk_option_stage(wl, flags):
     # 2.5e-3 .. 4.1e-3 over these cases; a wrong rotation, pairing, gamma or
     # norm is O(1))
     assert eq <= 1e-2 and ek <= 1e-2
+
+
+# The relative-position bias on the key-splitting 256-query attention kernel
+# (two wave groups in alternation) at a size it takes that is not a workload:
+# 512 query tiles, 64 x 128 image (table slices of 5 x 255 entries), every
+# option, plain and stressed; sampled pixels of the first and last sample.
+@pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
+@pytest.mark.parametrize("flags", ["relpos", "all"])
+def test_relpos_split_keys(flags, stress):
+    wl = Workload("bf16 d64 64x128 B2 n8", "bf16", 2, 512, 64, 128, 32, 8)
+    x, p, opts, out = run_case(wl, 57, stress, **OPT_FLAGS[flags])
+    x64, p64 = to_f64(x, p)
+    og = out.double().cpu().numpy().reshape(wl.B, wl.C, wl.T)
+    assert np.isfinite(og).all()
+    rng = np.random.default_rng(57)
+    worst = 0.0
+    for b in (0, wl.B - 1):
+        rows = np.unique(np.concatenate([[0, 255, 256, wl.T // 2 - 1, wl.T // 2, wl.T - 1],
+                                         rng.integers(0, wl.T, 10)]))
+        want = ORA.forward_pixels(x64, p64, wl.num_groups, wl.num_heads, b, rows, **options_f64(opts))
+        e = float(np.max(np.abs(og[b][:, rows] - want))) / float(np.max(np.abs(want)))
+        worst = max(worst, e)
+    print(f"  sampled err {worst:.3e}", flush=True)
+    assert worst <= TOL[wl.dtype]
