@@ -66,6 +66,12 @@
  *                              path: C % 64 == 0, T % 4 == 0); else empty
  *   qk32        (2, B, n, T, d) fp32 Q and K before the optional steps (bf16
  *                              problems without the rope region); else empty
+ *   attn_part   fp32 partial attention results (O, running max, row sums) of
+ *                              the query tiles whose keys are split over several
+ *                              work-groups (bf16, d in 33..64, T >= 1024 with T
+ *                              % 128 == 0, when the 256-query tiles leave a
+ *                              partial last round of at most half the compute
+ *                              units); else empty
  * After ssa_forward these hold the block's intermediates for inspection.
  */
 #ifndef SSA_H_
@@ -119,6 +125,7 @@ typedef struct {
   size_t o;
   size_t rope;         /* 0 bytes long when absent (offset of the next region) */
   size_t qk32;
+  size_t attn_part;
   int64_t gn_splits;   /* splits per (b, g) segment in gn_partial             */
   int64_t t_pad;       /* Tp: row pitch of vt in elements                     */
   int64_t d_pad;       /* dp: row pitch of q and k, rows per head of vt       */

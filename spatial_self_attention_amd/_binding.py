@@ -58,6 +58,7 @@ class WorkspaceLayout(ctypes.Structure):
         ("o", ctypes.c_size_t),
         ("rope", ctypes.c_size_t),
         ("qk32", ctypes.c_size_t),
+        ("attn_part", ctypes.c_size_t),
         ("gn_splits", ctypes.c_int64),
         ("t_pad", ctypes.c_int64),
         ("d_pad", ctypes.c_int64),

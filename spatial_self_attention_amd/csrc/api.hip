@@ -108,6 +108,9 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
   // that does (bf16 only: fp32 Q and K are written unrounded anyway).
   ws.rope = take(p->qk_fuse ? size_t(T * (d / 2)) * 8 : 0);
   ws.qk32 = take(dtype == SSA_BF16 && !p->qk_fuse ? size_t(2 * B * T * C) * 4 : 0);
+  plan_attention_tail(*p);
+  const int64_t tail = p->attn_split > 1 ? B * n * ((T + 255) / 256) - p->attn_full : 0;
+  ws.attn_part = take(size_t(tail * p->attn_split) * attn_part_bytes());
   ws.total = off;
   ws.gn_splits = p->splits;
   ws.t_pad = p->Tp;

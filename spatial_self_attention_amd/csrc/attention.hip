@@ -52,6 +52,10 @@ struct AttnParams {
   float scale;     // log2(e) / sqrt(d) (fp32 path; log2(e) with query/key normalisation)
   const void* rel; // ((2H-1)(2W-1), n) relative-position table, or NULL
   int H, W;
+  // key-splitting kernel: tiles [0, full) run whole, each later tile as
+  // `split` key ranges whose (O, m, l) go to `part` for attn_merge_kernel
+  int full, split;
+  float* part;
 };
 
 // ---------------------------------------------------------------------------
@@ -744,7 +748,17 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   const int half = lane >> 5, col = lane & 31;
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);  // key half
   const int gw = __builtin_amdgcn_readfirstlane(wave & 3);    // wave within the group
-  const int lid = xcd_remap(int(blockIdx.x), int(gridDim.x));
+  // Work-groups [0, full) take whole tiles and are dispatched first (one
+  // round or more of whole CUs); the rest take key ranges of the last tiles.
+  // Each part is remapped on its own so that consecutive ids share an XCD.
+  const int w = int(blockIdx.x);
+  int lid, piece = -1;
+  if (w < ap.full) {
+    lid = xcd_remap(w, ap.full);
+  } else {
+    piece = xcd_remap(w - ap.full, int(gridDim.x) - ap.full);
+    lid = ap.full + piece / ap.split;
+  }
   const int qtile = lid % ap.qtiles;
   const int bh = lid / ap.qtiles;
   const int head = bh % ap.n, b = bh / ap.n;
@@ -756,8 +770,17 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
 
   AttnState<D, 2> st;
   init_state<D, 2>(st, Q, qbase, T, half, col);
-  const int nh = T / KT / 2;  // key tiles per group
-  const int k0 = grp * nh * KT;
+  // The keys come in pairs of tiles, one tile of each pair per group; a key
+  // range is a run of pairs (ranges of one tile differ by at most one pair).
+  const int pairs = T / KT / 2;
+  int p0 = 0, p1 = pairs;
+  if (piece >= 0) {
+    const int i = piece % ap.split;
+    p0 = i * pairs / ap.split;
+    p1 = (i + 1) * pairs / ap.split;
+  }
+  const int nh = p1 - p0;  // key tiles per group (>= 1)
+  const int k0 = (2 * p0 + grp * nh) * KT;
   bf16* mine = lds + grp * NBUF * TL::BUF;
 
   // relative-position bias (REL = 2): the table column of the head, the
@@ -919,6 +942,7 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
       const float mx = fmaxf(st.m[qb], m1);
       const float w0 = __builtin_amdgcn_exp2f(st.m[qb] - mx), w1 = __builtin_amdgcn_exp2f(m1 - mx);
       st.l[qb] = st.l[qb] * w0 + l1 * w1;
+      st.m[qb] = mx;  // O and l are now relative to the common maximum
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -926,8 +950,95 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
           st.o[qb][db][r] =
               st.o[qb][db][r] * w0 + my[((qb * (D / 32) + db) * 16 + r) * 64 + lane] * w1;
     }
-    write_o<D, 2>(st, ap, b, head, qbase, half, col, lane,
-                  reinterpret_cast<bf16*>(stt + kState) + gw * 64 * (D + 8));
+    if (piece < 0) {
+      write_o<D, 2>(st, ap, b, head, qbase, half, col, lane,
+                    reinterpret_cast<bf16*>(stt + kState) + gw * 64 * (D + 8));
+    } else {
+      // this key range's (O, m, l): per wave, accumulator block c = (qb, db)
+      // as 64 lanes x 16 floats, then (m0, m1, l0, l1) per lane; 16-byte stores
+      float* pt = ap.part + (int64_t(piece) * 4 + gw) * (kO + 4) * 64;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = {st.o[qb][db][4 * g], st.o[qb][db][4 * g + 1], st.o[qb][db][4 * g + 2],
+                             st.o[qb][db][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(pt + ((qb * (D / 32) + db) * 64 + lane) * 16 + 4 * g) = v;
+          }
+      const f32x4 ml = {st.m[0], st.m[1], st.l[0], st.l[1]};
+      *reinterpret_cast<f32x4*>(pt + kO * 64 + lane * 4) = ml;
+    }
+  }
+}
+
+// Tiles cut into key ranges: the ranges' partial results are combined
+// (rescaled to their common maximum: the exact combination of softmax partial
+// sums) and O written.  A work-group per 64 queries of a tile (one wave of
+// the ranges' group 0); thread (c, lane) takes that lane's accumulator block
+// c = (qb, db), 16 registers stored contiguously: a thread's loads are
+// independent 16-byte loads, all in flight at once.
+template <int D>
+__global__ __launch_bounds__(64 * 2 * (D / 32)) void attn_merge_kernel(AttnParams ap) {
+  constexpr int kO = 2 * (D / 32) * 16;
+  constexpr int kMaxSplit = 8;
+  const int lane = threadIdx.x & 63, c = threadIdx.x >> 6;
+  const int qb = c / (D / 32), db = c % (D / 32);
+  const int half = lane >> 5, col = lane & 31;
+  const int j = int(blockIdx.x) >> 2, gw = int(blockIdx.x) & 3;  // tail tile, wave
+  const int lid = ap.full + j;
+  const int qtile = lid % ap.qtiles;
+  const int bh = lid / ap.qtiles;
+  const int head = bh % ap.n, b = bh / ap.n;
+  const int S = ap.split;
+  const int64_t stride = int64_t(4) * (kO + 4) * 64;  // floats per key range
+  const float* pt = ap.part + (int64_t(j) * S * 4 + gw) * (kO + 4) * 64;
+  const float* po = pt + (c * 64 + lane) * 16;  // this thread's 16 accumulators
+  const float* pm = pt + kO * 64 + lane * 4;     // (m0, m1, l0, l1)
+  f32x4 ml[kMaxSplit];
+#pragma unroll
+  for (int i = 0; i < kMaxSplit; ++i)
+    if (i < S) ml[i] = *reinterpret_cast<const f32x4*>(pm + i * stride);
+  float mx = ml[0][qb];
+#pragma unroll
+  for (int i = 1; i < kMaxSplit; ++i)
+    if (i < S) mx = fmaxf(mx, ml[i][qb]);
+  float acc[16], l = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxSplit; ++i) {
+    if (i < S) {
+      const float wgt = __builtin_amdgcn_exp2f(ml[i][qb] - mx);
+      l += ml[i][2 + qb] * wgt;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(po + i * stride + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * g + e] += v[e] * wgt;
+      }
+    }
+  }
+  const float inv = 1.0f / halves_sum(l);
+  // register 4g + e of block (qb, db) is query qb*32 + col, dim db*32 + 8g + 4*half + e
+  const int qi = qtile * 256 + gw * 64 + qb * 32 + col;
+  if (qi >= ap.T) return;
+  const int d = ap.d;
+  bf16* O = static_cast<bf16*>(ap.o) + (int64_t(b) * ap.T + qi) * ap.C + head * d;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int d0 = db * 32 + 8 * g + 4 * half;
+    if (d == D) {
+      bf16x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(acc[4 * g + e] * inv);
+      *reinterpret_cast<bf16x4*>(O + d0) = pk;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (d0 + e < d) O[d0 + e] = static_cast<bf16>(acc[4 * g + e] * inv);
+    }
   }
 }
 
@@ -1073,6 +1184,24 @@ bool rel_slice_fits(int QT, int KT, int W) {
   return spans * (2 * int64_t(W) - 1) <= kRelSlice;
 }
 
+// The key-splitting kernel over 256-query tiles, with the tiles of a partial
+// last round cut into key ranges when the plan says so (then the merge
+// kernel follows on the same stream).
+void launch_pp(const Plan& p, AttnParams ap, int64_t t256, hipStream_t stream) {
+  typedef Tile<64, 2, 64, 4> TL;
+  ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
+  const int split = p.attn_split;
+  const int64_t full = split > 1 ? p.attn_full : t256;
+  const int64_t grid = full + (t256 - full) * split;
+  ap.full = int(full);
+  ap.split = split;
+  if (ap.rel != nullptr)
+    attnpp_bf16_kernel<64, 64, 2><<<dim3(unsigned(grid)), 512, 0, stream>>>(ap);
+  else
+    attnpp_bf16_kernel<64, 64, 0><<<dim3(unsigned(grid)), 512, 0, stream>>>(ap);
+  if (split > 1) attn_merge_kernel<64><<<dim3(unsigned((t256 - full) * 4)), 256, 0, stream>>>(ap);
+}
+
 void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream) {
   if (p.T >= 1024) {
     const int64_t t512 = bh * ((p.T + 511) / 512), t256 = bh * ((p.T + 255) / 256);
@@ -1081,8 +1210,9 @@ void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream
       return;
     }
     // (the one-block kernel's relative-position variant runs two work-groups
-    // per CU, so a single round of 256-query tiles already pays for it)
-    if (t256 >= (ap.rel != nullptr ? 1 : 2) * int64_t(p.cus)) {
+    // per CU, so a single round of 256-query tiles already pays for it; with
+    // the last round's tiles cut into key ranges, so does the plain kernel)
+    if (t256 >= (ap.rel != nullptr || p.attn_split > 1 ? 1 : 2) * int64_t(p.cus)) {
       // 256-query tiles.  With an even number of full key tiles each tile runs
       // as one 8-wave work-group whose halves split the keys (attnpp): faster
       // per tile than two 4-wave work-groups sharing a CU, and a partial last
@@ -1090,12 +1220,7 @@ void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream
       // per CU.  The relative-position bias takes the same kernel where its
       // table slices fit.
       if (p.T % 128 == 0 && (ap.rel == nullptr || rel_slice_fits(256, 64, ap.W))) {
-        typedef Tile<64, 2, 64, 4> TL;
-        ap.qtiles = int((ap.T + TL::QT - 1) / TL::QT);
-        if (ap.rel != nullptr)
-          attnpp_bf16_kernel<64, 64, 2><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
-        else
-          attnpp_bf16_kernel<64, 64, 0><<<dim3(unsigned(t256)), 512, 0, stream>>>(ap);
+        launch_pp(p, ap, t256, stream);
         return;
       }
       if (ap.rel == nullptr) {
@@ -1108,6 +1233,27 @@ void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream
 }
 
 }  // namespace
+
+// The key-splitting kernel's partial last round (bf16, dp = 64, T >= 1024,
+// T % 128 == 0, at least one round of 256-query tiles): when its r tiles
+// fill at most half the CUs, each is cut into S = min(cus / r, 8, T / 128)
+// key ranges, so that the last round takes about 1/S of a tile's time.
+void plan_attention_tail(Plan& p) {
+  p.attn_split = 1;
+  p.attn_full = 0;
+  if (p.dtype != SSA_BF16 || p.dp != 64 || p.T < 1024 || p.T % 128 != 0) return;
+  const int64_t cus = p.cus;
+  const int64_t t256 = p.B * p.n * ((p.T + 255) / 256);
+  const int64_t r = t256 % cus;
+  if (t256 < cus || r == 0 || 2 * r > cus) return;
+  int64_t s = cus / r;
+  if (s > 8) s = 8;
+  if (s > p.T / 128) s = p.T / 128;
+  p.attn_split = int(s);
+  p.attn_full = t256 - r;
+}
+
+size_t attn_part_bytes() { return size_t(4) * 64 * (2 * (64 / 32) * 16 + 4) * sizeof(float); }
 
 hipError_t launch_attention(const Plan& p, const Args& a) {
   AttnParams ap{};
@@ -1128,6 +1274,9 @@ hipError_t launch_attention(const Plan& p, const Args& a) {
   ap.rel = a.rel_pos_table;
   ap.H = int(p.H);
   ap.W = int(p.W);
+  ap.full = 0;
+  ap.split = 1;
+  ap.part = reinterpret_cast<float*>(a.ws + p.ws.attn_part);
   const int64_t bh = p.B * p.n;
   if (p.dtype == SSA_BF16) {
     // one 256-query work-group per head when the heads alone fill the chip

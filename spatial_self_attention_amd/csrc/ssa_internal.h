@@ -49,6 +49,13 @@ struct Plan {
   // epilogue (qkv_main and d in {16, 32, 64, 128}); otherwise the projection
   // writes fp32 Q and K to the qk32 region and one pass applies them
   bool qk_fuse;
+  // attention on 256-query tiles that split their keys between the two
+  // halves of a work-group: the first attn_full tiles run whole; each of the
+  // rest (a partial last round of at most half the compute units) is cut into
+  // attn_split key ranges whose partial results are merged afterwards
+  // (attn_split == 1: every tile whole)
+  int attn_split;
+  int64_t attn_full;
   ssa_workspace_layout ws;
 };
 
@@ -78,6 +85,11 @@ hipError_t launch_qk_post(const Plan& p, const Args& a);
 hipError_t launch_rope_table(const Plan& p, const Args& a);
 // Zeros in the padding columns d .. dp-1 of the q and k layouts (bf16, dp > d).
 hipError_t launch_zero_pad(const Plan& p, const Args& a);
+
+// Fills p.attn_split and p.attn_full from the sizes and p.cus.
+void plan_attention_tail(Plan& p);
+// Bytes of the attn_part region per split key range.
+size_t attn_part_bytes();
 
 // Launchers (one per stage); each returns hipSuccess or the launch error.
 hipError_t launch_gn_stats(const Plan& p, const Args& a);

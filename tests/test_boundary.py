@@ -48,6 +48,16 @@ def _layout_expect(B, C, H, W, G, n, esize):
     dp = d if esize == 4 else -(-d // 32) * 32      # bf16 heads padded to a multiple of 32
     Tp = (T + 63) // 64 * 64
     fuse = esize == 2 and C % 64 == 0 and T % 4 == 0 and d in (16, 32, 64, 128)
+    # partial (O, m, l) of the key ranges of a partial last round of 256-query
+    # tiles (bf16 heads padded to 64, T >= 1024, T % 128 == 0; sized for 256
+    # compute units, the count assumed where no device is visible): r tiles
+    # filling at most half the units, each cut into min(256 // r, 8, T // 128)
+    # ranges of 4 waves x 64 lanes x 68 floats
+    part = 0
+    t256 = B * n * -(-T // 256)
+    r = t256 % 256
+    if esize == 2 and dp == 64 and T >= 1024 and T % 128 == 0 and t256 >= 256 and 0 < 2 * r <= 256:
+        part = r * min(256 // r, 8, T // 128) * 4 * 64 * 68 * 4
     return {
         "gn_stats": B * G * 8, "gn_coef": B * C * 8,
         "q": B * n * T * dp * esize, "k": B * n * T * dp * esize,
@@ -56,6 +66,7 @@ def _layout_expect(B, C, H, W, G, n, esize):
         # optional steps, else fp32 Q and K for the separate pass (bf16 only)
         "rope": T * (d // 2) * 8 if fuse else 0,
         "qk32": 2 * B * T * C * 4 if (esize == 2 and not fuse) else 0,
+        "attn_part": part,
         "d_pad": dp,
     }
 
@@ -71,6 +82,9 @@ def _layout_expect(B, C, H, W, G, n, esize):
     (2, 4, 1, 1, 4, 2, ssa.SSA_BF16),      # d = 2, padded to 32
     (2, 192, 8, 8, 8, 4, ssa.SSA_BF16),    # d = 48, padded to 64
     (2, 128, 8, 8, 8, 8, ssa.SSA_BF16),    # d = 16, padded to 32
+    (2, 576, 64, 64, 32, 9, ssa.SSA_BF16),   # 288 tiles: the last 32 in 8 key ranges
+    (1, 1088, 66, 64, 32, 17, ssa.SSA_BF16), # 289 tiles: the last 33 in 7 key ranges
+    (3, 640, 64, 64, 32, 10, ssa.SSA_BF16),  # 480 tiles: a last round above half the CUs
 ])
 def test_workspace_layout(shape):
     B, C, H, W, G, n, dt = shape
@@ -80,11 +94,13 @@ def test_workspace_layout(shape):
     want = _layout_expect(B, C, H, W, G, n, esize)
     assert lay["d_pad"] == want.pop("d_pad")
     want["gn_partial"] = B * G * lay["gn_splits"] * 16
-    order = ["gn_partial", "gn_stats", "gn_coef", "q", "k", "vt", "o", "rope", "qk32"]
+    order = ["gn_partial", "gn_stats", "gn_coef", "q", "k", "vt", "o", "rope", "qk32", "attn_part"]
     for a, b in zip(order, order[1:]):
         assert lay[a] % 256 == 0
         assert lay[a] + want[a] <= lay[b], (a, b)
-    assert lay["qk32"] + want["qk32"] <= lay["total"]
+    assert lay["attn_part"] + want["attn_part"] <= lay["total"]
+    # regions of zero bytes take no space: the total is the end of the last non-empty one
+    assert lay["total"] - (lay["attn_part"] + want["attn_part"]) < 256
     assert lay["t_pad"] % 64 == 0 and lay["t_pad"] >= H * W
     assert lay["gn_splits"] >= 1
     # every chunk of a segment is non-empty

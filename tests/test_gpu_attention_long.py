@@ -3,7 +3,10 @@ covering each kernel shape the stage picks there: the two-query-block kernel
 with 512-query work-groups (key tiles of 128) or 256-query work-groups (key
 tiles of 64: 8-wave work-groups that split the keys in halves and merge in
 LDS when the sequence is a multiple of 128 (T = 9216, 8320), two 4-wave
-work-groups per CU otherwise (T = 9215, 9280)), and the one-block kernel when the query
+work-groups per CU otherwise (T = 9215, 9280)), the same 8-wave kernel with
+the tiles of a partial last round cut into 4, 7 or 8 key ranges whose
+partial results a second kernel merges (one round of tiles and a last round
+filling at most half the CUs), and the one-block kernel when the query
 tiles are too few to fill whole rounds of the CUs (the choice assumes
 MI355X's 256 CUs).
 
@@ -72,7 +75,11 @@ def run_attention(B, n, H, W, seed, kind):
 CASES = [
     # (B, n, H, W, rows sampled per head or None for all)
     (1, 5, 33, 40, None),     # one-block kernel; T % 128 = 40
-    (4, 5, 64, 64, 64),       # the LDM level-1 workload's shape: one-block kernel
+    (4, 5, 64, 64, 64),       # the LDM level-1 workload's shape: 320 tiles of 256, the last
+                              # 64 each cut into 4 key ranges
+    (2, 9, 64, 64, 40),       # 288 tiles: the last 32 in 8 key ranges of 2 tile pairs
+    (1, 17, 66, 64, 40),      # 289 tiles, T % 256 = 128: the last 33 in 7 uneven key ranges
+    (1, 5, 32, 32, None),     # 20 tiles: one-block kernel
     (1, 32, 63, 63, 40),      # 256 query tiles of 512: T % 128 = 1, last tile 385 rows
     (2, 16, 64, 64, 48),      # 256 query tiles of 512, even sizes
     (2, 10, 95, 97, 40),      # 720 query tiles of 256: T % 64 = 63
