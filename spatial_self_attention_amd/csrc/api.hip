@@ -70,16 +70,19 @@ ssa_status make_plan(int64_t B, int64_t C, int64_t H, int64_t W, int64_t G,
 
   // Statistics split.  With enough (b, g) segments to fill the chip and
   // segments a work-group streams quickly, one work-group per segment also
-  // finalises the statistics (one kernel).  Otherwise each segment is cut into
-  // chunks of at least 8192 elements, about 2048 work-groups in all, and a
-  // second kernel merges them.
+  // finalises the statistics (one kernel); likewise, with a wider work-group,
+  // for longer or fewer segments down to a quarter as many as CUs (vector
+  // loads only).  Otherwise each segment is cut into chunks of at least 8192
+  // elements, about 2048 work-groups in all, and a second kernel merges them.
   const int64_t L = (C / G) * T;
   const int vec = 16 / p->esize;
   p->gn_vec = (L % vec == 0) ? vec : 1;
   p->seg_len = L;
   int64_t segs = B * G;
   int64_t splits = 1;
-  if (segs < 256 || L > 65536) {
+  p->gn_seg = (segs < 256 || L > 65536) && p->gn_vec == vec && 4 * segs >= p->cus &&
+              L <= (int64_t(1) << 20);
+  if ((segs < 256 || L > 65536) && !p->gn_seg) {
     const int64_t want = (2048 + segs - 1) / segs;
     const int64_t cap = (L + 8191) / 8192;
     splits = want < cap ? want : cap;

@@ -18,6 +18,10 @@
 //   gn_finalize_kernel      grid B*G: one wave merges the chunks of a segment
 //       and emits the same statistics and coefficients.
 //   gn_stats_wave_kernel    many short segments: one wave per segment.
+//   gn_seg_kernel           long segments, at least a quarter as many as CUs:
+//       one 512-thread work-group per segment with eight 16-byte loads in
+//       flight per thread, finalising in place (one kernel instead of the split
+//       pass and its merge).
 #include "ssa_internal.h"
 
 namespace ssa {
@@ -203,6 +207,66 @@ __global__ __launch_bounds__(256) void gn_stats_wave_kernel(const T* __restrict_
   finalize<T>(acc, int(seg), gamma, beta, stats, coef, G, Cg, C, lane, 64);
 }
 
+// One work-group of NT threads per segment, UNR 16-byte loads in flight per
+// thread; the waves' (count, mean, M2) merged through LDS, then finalised.
+template <typename T, int VEC, int NT, int UNR>
+__global__ __launch_bounds__(NT) void gn_seg_kernel(const T* __restrict__ x, int64_t seg_len,
+                                                    const T* __restrict__ gamma,
+                                                    const T* __restrict__ beta,
+                                                    float2* __restrict__ stats,
+                                                    float2* __restrict__ coef, int G, int Cg, int C) {
+  typedef typename VecOf<T, VEC>::type V;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x;
+  const T* base = x + seg * seg_len;
+  const float x0 = to_f32(base[0]);
+  const V* vb = reinterpret_cast<const V*>(base);
+  const int64_t nv = seg_len / VEC;
+  float sd = 0.f, sq = 0.f;
+  int cnt = 0;
+  int64_t i = tid;
+  for (; i + (UNR - 1) * NT < nv; i += UNR * NT) {
+    V v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) v[u] = vb[i + u * NT];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float d = to_f32(v[u][e]) - x0;
+        sd += d;
+        sq = fmaf(d, d, sq);
+      }
+    cnt += UNR * VEC;
+  }
+  for (; i < nv; i += NT) {
+    const V v = vb[i];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float d = to_f32(v[e]) - x0;
+      sd += d;
+      sq = fmaf(d, d, sq);
+    }
+    cnt += VEC;
+  }
+  Moments acc{0.f, 0.f, 0.f};
+  if (cnt > 0) {
+    const float n = float(cnt);
+    const float md = sd / n;
+    acc = Moments{n, x0 + md, fmaxf(sq - sd * md, 0.f)};
+  }
+  acc = wave_merge(acc);
+  __shared__ Moments waves[NW];
+  const int wave = tid / 64;
+  if ((tid & 63) == 0) waves[wave] = acc;
+  __syncthreads();
+  Moments r = waves[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = merge(r, waves[w]);
+  finalize<T>(r, int(seg), gamma, beta, stats, coef, G, Cg, C, tid, NT);
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void gn_finalize_kernel(const float4* __restrict__ partial,
                                                          int splits, const T* __restrict__ gamma,
@@ -232,6 +296,11 @@ hipError_t launch_vec(const Plan& p, const Args& a) {
   const int G = int(p.G), Cg = int(p.C / p.G), C = int(p.C);
   dim3 grid(unsigned(p.splits * p.B * p.G));
   if constexpr (VEC > 1) {
+    if (p.gn_seg) {
+      gn_seg_kernel<T, VEC, 512, 8><<<dim3(unsigned(p.B * p.G)), 512, 0, a.stream>>>(
+          x, p.seg_len, gamma, beta, stats, coef, G, Cg, C);
+      return hipGetLastError();
+    }
     if (p.splits == 1 && p.seg_len <= kWaveSeg && p.B * p.G >= 4 * int64_t(p.cus)) {
       const int64_t segs = p.B * p.G;
       gn_stats_wave_kernel<T, VEC><<<dim3(unsigned((segs + 3) / 4)), 256, 0, a.stream>>>(

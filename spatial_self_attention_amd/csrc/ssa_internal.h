@@ -41,6 +41,7 @@ struct Plan {
   // elements is cut into `splits` chunks of `chunk` elements.
   int64_t seg_len, chunk, splits;
   int gn_vec;      // elements per vector load in the stats pass (1 = scalar)
+  bool gn_seg;     // one 512-thread work-group per segment (splits == 1)
   int cus;         // compute units of the current device (launch shaping)
   // bf16 Q/K/V projection on the 128 x 128 MFMA kernel (C % 64 == 0,
   // T % 4 == 0, d % 8 == 0); otherwise the general tile kernel

@@ -237,15 +237,26 @@ def test_full_size_sampled(idx, stress):
     assert worst <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_gn_statistics_full_size(idx):
-    """GroupNorm statistics and coefficients of every (b, g) at the full
-    workload sizes, one for each statistics launch shape: one wave per segment
-    (workload 1: 2048 short segments), one work-group per segment with the
-    finalise fused (workload 2), split segments merged by a second kernel
-    (workloads 3 and 4)."""
-    wl = WORKLOADS[idx]
-    x, p, _, ws = run(wl, 1100 + idx)
+GN_SHAPES = [
+    # (name or workload index, seed)
+    (1, 1101),   # one wave per segment (2048 short segments)
+    (2, 1102),   # one 256-thread work-group per segment, finalised in place
+    (3, 1103),   # one 512-thread work-group per segment (128 segments of 40960)
+    (4, 1104),   # the same with 64 segments of 184320
+    (Workload("split bf16 B1 C320 48x48", "bf16", 1, 320, 48, 48, 32, 5), 1105),
+    # 32 segments: chunks merged by a second kernel
+    (Workload("seg fp32 B2 C256 16x16", "f32", 2, 256, 16, 16, 32, 4), 1106),
+    # fp32, 64 segments: one 512-thread work-group per segment, 4-float loads
+]
+
+
+@pytest.mark.parametrize("case", GN_SHAPES, ids=lambda c: str(c[0]) if isinstance(c[0], int) else c[0].name)
+def test_gn_statistics_full_size(case):
+    """GroupNorm statistics and coefficients of every (b, g), one case for
+    each statistics launch shape (the choice assumes MI355X's 256 CUs), at
+    the full workload sizes where a workload takes that shape."""
+    wl = WORKLOADS[case[0]] if isinstance(case[0], int) else case[0]
+    x, p, _, ws = run(wl, case[1])
     x64, p64 = to_f64(x, p)
     _, mean, var = ORA.group_norm(x64, p64["norm_weight"], p64["norm_bias"], wl.num_groups)
     rstd = 1.0 / np.sqrt(var + 1e-5)
