@@ -92,9 +92,11 @@ def stage_work(wl):
 
 # Kernel names (as rocprofv3 prints them) behind each stage, for the counters.
 STAGE_KERNELS = {
-    "gn_stats": "gn_stats_kernel (+ gn_finalize_kernel when segments are split)",
+    "gn_stats": "gn_stats_wave_kernel / gn_stats_kernel / gn_seg_kernel (+ gn_finalize_kernel "
+                "when segments are split)",
     "qkv": "gemm_bf16_kernel<0, *>",
-    "attention": "attn_bf16_kernel / attn2_bf16_kernel / attnpp_bf16_kernel",
+    "attention": "attn_bf16_kernel / attn2_bf16_kernel / attnpp_bf16_kernel (+ attn_merge_kernel "
+                 "when the tiles of a partial last round are cut into key ranges)",
     "qkv_attention": "fused_bf16_kernel",
     "out_proj": "gemm_bf16_kernel<1, 0>",
 }
