@@ -42,16 +42,20 @@ struct RopeTabParams {
   float theta[kMaxHalf];
 };
 
-// grid (ceil(T / 64), d/2): block y is pair i (theta_i read with a uniform
-// index), lane x token t.
-__global__ __launch_bounds__(64) void rope_table_kernel(RopeTabParams rp) {
-  const int i = blockIdx.y;
-  const int t = blockIdx.x * 64 + threadIdx.x;
-  if (t >= rp.T) return;
-  const float ang = float(t) * rp.theta[i];  // one float32 product
-  float s, c;
-  sincosf(ang, &s, &c);
-  rp.tab[int64_t(t) * rp.hd + i] = make_float2(c, s);
+// One thread per table entry (t, i), i fastest, so that the stores are
+// consecutive; theta is staged in LDS for the per-lane index.
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTabParams rp) {
+  __shared__ float th[kMaxHalf];
+  if (int(threadIdx.x) < rp.hd) th[threadIdx.x] = rp.theta[threadIdx.x];
+  __syncthreads();
+  const int64_t total = int64_t(rp.T) * rp.hd;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total; e += int64_t(gridDim.x) * 256) {
+    const int t = int(e / rp.hd), i = int(e - int64_t(t) * rp.hd);
+    const float ang = float(t) * th[i];  // one float32 product
+    float s, c;
+    sincosf(ang, &s, &c);
+    rp.tab[e] = make_float2(c, s);
+  }
 }
 
 struct ZeroPadParams {
@@ -183,8 +187,9 @@ hipError_t launch_rope_table(const Plan& p, const Args& a) {
   rp.T = int(p.T);
   rp.hd = int(p.d / 2);
   fill_theta(rp.theta, p.d);
-  const dim3 grid(unsigned((p.T + 63) / 64), unsigned(rp.hd));
-  rope_table_kernel<<<grid, 64, 0, a.stream>>>(rp);
+  const int64_t total = p.T * int64_t(rp.hd);
+  const int64_t blocks = (total + 255) / 256;
+  rope_table_kernel<<<dim3(unsigned(blocks < 4096 ? blocks : 4096)), 256, 0, a.stream>>>(rp);
   return hipGetLastError();
 }
 

@@ -264,13 +264,22 @@ def test_qk_option_stage(wl, flags):
 
 
 # The relative-position bias on the key-splitting 256-query attention kernel
-# (two wave groups in alternation) at a size it takes that is not a workload:
-# 512 query tiles, 64 x 128 image (table slices of 5 x 255 entries), every
-# option, plain and stressed; sampled pixels of the first and last sample.
+# (two wave groups in alternation) at sizes it takes that are not workloads:
+# 512 query tiles, 64 x 128 image (table slices of 5 x 255 entries); and 272
+# tiles of a 64 x 64 image, whose last 16 (the last sample's last heads) are
+# cut into 8 key ranges each and merged (the choice assumes MI355X's 256
+# CUs); every option, plain and stressed; sampled pixels of the first and
+# last sample.
+SPLIT_SHAPES = [
+    Workload("bf16 d64 64x128 B2 n8", "bf16", 2, 512, 64, 128, 32, 8),
+    Workload("bf16 d64 64x64 B1 n17 last round in key ranges", "bf16", 1, 1088, 64, 64, 32, 17),
+]
+
+
 @pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
 @pytest.mark.parametrize("flags", ["relpos", "all"])
-def test_relpos_split_keys(flags, stress):
-    wl = Workload("bf16 d64 64x128 B2 n8", "bf16", 2, 512, 64, 128, 32, 8)
+@pytest.mark.parametrize("wl", SPLIT_SHAPES, ids=lambda w: w.name)
+def test_relpos_split_keys(wl, flags, stress):
     x, p, opts, out = run_case(wl, 57, stress, **OPT_FLAGS[flags])
     x64, p64 = to_f64(x, p)
     og = out.double().cpu().numpy().reshape(wl.B, wl.C, wl.T)
