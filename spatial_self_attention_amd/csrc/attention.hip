@@ -318,8 +318,7 @@ __device__ __forceinline__ void write_o(const AttnState<D, QB>& st, const AttnPa
       const int q = c / CPR, dc = c % CPR;
       const int qi = qbase + q;
       if (qi < ap.T)
-        *reinterpret_cast<bf16x8*>(O + int64_t(qi) * ap.C + dc * 8) =
-            *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]);
+        store_nt(O + int64_t(qi) * ap.C + dc * 8, *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]));
     }
   } else {
     for (int i = 0; i < QB * D / 16; ++i) {
@@ -965,10 +964,10 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
           for (int g = 0; g < 4; ++g) {
             const f32x4 v = {st.o[qb][db][4 * g], st.o[qb][db][4 * g + 1], st.o[qb][db][4 * g + 2],
                              st.o[qb][db][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(pt + ((qb * (D / 32) + db) * 64 + lane) * 16 + 4 * g) = v;
+            store_nt(pt + ((qb * (D / 32) + db) * 64 + lane) * 16 + 4 * g, v);
           }
       const f32x4 ml = {st.m[0], st.m[1], st.l[0], st.l[1]};
-      *reinterpret_cast<f32x4*>(pt + kO * 64 + lane * 4) = ml;
+      store_nt(pt + kO * 64 + lane * 4, ml);
     }
   }
 }
@@ -1033,7 +1032,7 @@ __global__ __launch_bounds__(64 * 2 * (D / 32)) void attn_merge_kernel(AttnParam
       bf16x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(acc[4 * g + e] * inv);
-      *reinterpret_cast<bf16x4*>(O + d0) = pk;
+      store_nt(O + d0, pk);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)

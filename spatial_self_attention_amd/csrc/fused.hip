@@ -505,8 +505,7 @@ __global__ __launch_bounds__(FNT, 1) void fused_bf16_kernel(FusedParams fp) {
       const int q = c / CPR, dc = c % CPR;
       const int qi = wave * 32 + q;
       if (qi < T)
-        *reinterpret_cast<bf16x8*>(O + int64_t(qi) * C + dc * 8) =
-            *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]);
+        store_nt(O + int64_t(qi) * C + dc * 8, *reinterpret_cast<const bf16x8*>(&stg[q * EP + dc * 8]));
     }
   }
 }

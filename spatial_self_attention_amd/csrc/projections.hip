@@ -807,8 +807,8 @@ __device__ __forceinline__ void epi_store_qkopt(const ProjParams& pp, bf16* lds0
         pb[e] = static_cast<bf16>(b[e] * sc);
       }
       bf16* row = dst + (int64_t(bs * pp.n + head) * T + t) * pp.dp;
-      *reinterpret_cast<bf16x8*>(row + ic * 8) = pa;
-      *reinterpret_cast<bf16x8*>(row + d / 2 + ic * 8) = pb;
+      store_nt(row + ic * 8, pa);
+      store_nt(row + d / 2 + ic * 8, pb);
     }
   }
 }
@@ -861,7 +861,7 @@ __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp
         bf16x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(xv[e] + y[e]);
-        *reinterpret_cast<bf16x4*>(out + idx) = pk;
+        store_nt(out + idx, pk);
       }
     } else {
       const bf16* E = stg;
@@ -873,8 +873,8 @@ __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp
         const int cl = 4 * u + (lane >> 4);
         const int c = cw + cl;
         const int head = int(unsigned(c) / unsigned(pp.d)), dd = c - head * pp.d;
-        *reinterpret_cast<bf16x4*>(vt + (int64_t(b * pp.n + head) * pp.dp + dd) * pp.Tp + slot) =
-            *reinterpret_cast<const bf16x4*>(&E[cl * EPB + 4 * tq]);
+        store_nt(vt + (int64_t(b * pp.n + head) * pp.dp + dd) * pp.Tp + slot,
+                 *reinterpret_cast<const bf16x4*>(&E[cl * EPB + 4 * tq]));
       }
     }
   } else {
@@ -896,8 +896,8 @@ __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp
         while (t >= T) { t -= T; ++b; }
       }
       if (nn < pp.NT)
-        *reinterpret_cast<bf16x8*>(dst + (int64_t(b * pp.n + head) * T + t) * pp.dp + dd) =
-            *reinterpret_cast<const bf16x8*>(&E[(r0 + 8 * u) * EPB + q8 * 8]);
+        store_nt(dst + (int64_t(b * pp.n + head) * T + t) * pp.dp + dd,
+                 *reinterpret_cast<const bf16x8*>(&E[(r0 + 8 * u) * EPB + q8 * 8]));
     }
   }
 }

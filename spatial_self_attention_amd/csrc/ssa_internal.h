@@ -104,6 +104,21 @@ hipError_t launch_out_proj(const Plan& p, const Args& a);
 bool fused_available(const Plan& p);
 hipError_t launch_fused(const Plan& p, const Args& a);
 
+// Stores of write-once streams (Q, K, V^T, O, partial results, the block's
+// output): non-temporal, so that they do not evict from L2 the operands that
+// other work-groups of the same launch still re-read (weight panels, key
+// tiles, x).  8- or 16-byte values.
+typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+template <typename V>
+__device__ __forceinline__ void store_nt(void* p, const V& v) {
+  static_assert(sizeof(V) == 8 || sizeof(V) == 16, "8- or 16-byte stores");
+  if constexpr (sizeof(V) == 16)
+    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, v), static_cast<nt_u32x4*>(p));
+  else
+    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x2, v), static_cast<nt_u32x2*>(p));
+}
+
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
 
