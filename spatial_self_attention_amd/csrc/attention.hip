@@ -954,7 +954,8 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
                     reinterpret_cast<bf16*>(stt + kState) + gw * 64 * (D + 8));
     } else {
       // this key range's (O, m, l): per wave, accumulator block c = (qb, db)
-      // as 64 lanes x 16 floats, then (m0, m1, l0, l1) per lane; 16-byte stores
+      // as 64 lanes x 16 floats, then (m0, m1, l0, l1) per lane; 16-byte
+      // stores, cached (the merge kernel reads them next)
       float* pt = ap.part + (int64_t(piece) * 4 + gw) * (kO + 4) * 64;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -964,10 +965,10 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
           for (int g = 0; g < 4; ++g) {
             const f32x4 v = {st.o[qb][db][4 * g], st.o[qb][db][4 * g + 1], st.o[qb][db][4 * g + 2],
                              st.o[qb][db][4 * g + 3]};
-            store_nt(pt + ((qb * (D / 32) + db) * 64 + lane) * 16 + 4 * g, v);
+            *reinterpret_cast<f32x4*>(pt + ((qb * (D / 32) + db) * 64 + lane) * 16 + 4 * g) = v;
           }
       const f32x4 ml = {st.m[0], st.m[1], st.l[0], st.l[1]};
-      store_nt(pt + kO * 64 + lane * 4, ml);
+      *reinterpret_cast<f32x4*>(pt + kO * 64 + lane * 4) = ml;
     }
   }
 }

@@ -104,10 +104,11 @@ hipError_t launch_out_proj(const Plan& p, const Args& a);
 bool fused_available(const Plan& p);
 hipError_t launch_fused(const Plan& p, const Args& a);
 
-// Stores of write-once streams (Q, K, V^T, O, partial results, the block's
-// output): non-temporal, so that they do not evict from L2 the operands that
-// other work-groups of the same launch still re-read (weight panels, key
-// tiles, x).  8- or 16-byte values.
+// Stores of write-once streams (Q, K, V^T, O, the block's output):
+// non-temporal, so that they do not evict from L2 the operands that other
+// work-groups of the same launch still re-read (weight panels, key tiles, x).
+// Not for data the next kernel reads at once (the attention partials): those
+// are read back faster when written through the caches.  8- or 16-byte values.
 typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
 template <typename V>
