@@ -978,11 +978,11 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
 // sums) and O written.  A work-group per 64 queries of a tile (one wave of
 // the ranges' group 0); thread (c, lane) takes that lane's accumulator block
 // c = (qb, db), 16 registers stored contiguously: a thread's loads are
-// independent 16-byte loads, all in flight at once.
-template <int D>
+// independent 16-byte loads, all in flight at once (S, the number of ranges,
+// is a template parameter so that none of them waits behind a branch).
+template <int D, int S>
 __global__ __launch_bounds__(64 * 2 * (D / 32)) void attn_merge_kernel(AttnParams ap) {
   constexpr int kO = 2 * (D / 32) * 16;
-  constexpr int kMaxSplit = 8;
   const int lane = threadIdx.x & 63, c = threadIdx.x >> 6;
   const int qb = c / (D / 32), db = c % (D / 32);
   const int half = lane >> 5, col = lane & 31;
@@ -991,34 +991,31 @@ __global__ __launch_bounds__(64 * 2 * (D / 32)) void attn_merge_kernel(AttnParam
   const int qtile = lid % ap.qtiles;
   const int bh = lid / ap.qtiles;
   const int head = bh % ap.n, b = bh / ap.n;
-  const int S = ap.split;
   const int64_t stride = int64_t(4) * (kO + 4) * 64;  // floats per key range
   const float* pt = ap.part + (int64_t(j) * S * 4 + gw) * (kO + 4) * 64;
   const float* po = pt + (c * 64 + lane) * 16;  // this thread's 16 accumulators
   const float* pm = pt + kO * 64 + lane * 4;     // (m0, m1, l0, l1)
-  f32x4 ml[kMaxSplit];
+  f32x4 ml[S], ov[S][4];
 #pragma unroll
-  for (int i = 0; i < kMaxSplit; ++i)
-    if (i < S) ml[i] = *reinterpret_cast<const f32x4*>(pm + i * stride);
+  for (int i = 0; i < S; ++i) {
+    ml[i] = *reinterpret_cast<const f32x4*>(pm + i * stride);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ov[i][g] = *reinterpret_cast<const f32x4*>(po + i * stride + 4 * g);
+  }
   float mx = ml[0][qb];
 #pragma unroll
-  for (int i = 1; i < kMaxSplit; ++i)
-    if (i < S) mx = fmaxf(mx, ml[i][qb]);
+  for (int i = 1; i < S; ++i) mx = fmaxf(mx, ml[i][qb]);
   float acc[16], l = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxSplit; ++i) {
-    if (i < S) {
-      const float wgt = __builtin_amdgcn_exp2f(ml[i][qb] - mx);
-      l += ml[i][2 + qb] * wgt;
+  for (int i = 0; i < S; ++i) {
+    const float wgt = __builtin_amdgcn_exp2f(ml[i][qb] - mx);
+    l += ml[i][2 + qb] * wgt;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(po + i * stride + 4 * g);
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * g + e] += v[e] * wgt;
-      }
-    }
+      for (int e = 0; e < 4; ++e) acc[4 * g + e] += ov[i][g][e] * wgt;
   }
   const float inv = 1.0f / halves_sum(l);
   // register 4g + e of block (qb, db) is query qb*32 + col, dim db*32 + 8g + 4*half + e
@@ -1199,7 +1196,18 @@ void launch_pp(const Plan& p, AttnParams ap, int64_t t256, hipStream_t stream) {
     attnpp_bf16_kernel<64, 64, 2><<<dim3(unsigned(grid)), 512, 0, stream>>>(ap);
   else
     attnpp_bf16_kernel<64, 64, 0><<<dim3(unsigned(grid)), 512, 0, stream>>>(ap);
-  if (split > 1) attn_merge_kernel<64><<<dim3(unsigned((t256 - full) * 4)), 256, 0, stream>>>(ap);
+  if (split > 1) {
+    const dim3 mg(unsigned((t256 - full) * 4));
+    switch (split) {  // 2 .. 8
+      case 2: attn_merge_kernel<64, 2><<<mg, 256, 0, stream>>>(ap); break;
+      case 3: attn_merge_kernel<64, 3><<<mg, 256, 0, stream>>>(ap); break;
+      case 4: attn_merge_kernel<64, 4><<<mg, 256, 0, stream>>>(ap); break;
+      case 5: attn_merge_kernel<64, 5><<<mg, 256, 0, stream>>>(ap); break;
+      case 6: attn_merge_kernel<64, 6><<<mg, 256, 0, stream>>>(ap); break;
+      case 7: attn_merge_kernel<64, 7><<<mg, 256, 0, stream>>>(ap); break;
+      default: attn_merge_kernel<64, 8><<<mg, 256, 0, stream>>>(ap); break;
+    }
+  }
 }
 
 void launch_bf16_64(const Plan& p, AttnParams ap, int64_t bh, hipStream_t stream) {
