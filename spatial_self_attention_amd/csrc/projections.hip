@@ -570,7 +570,10 @@ __device__ __forceinline__ void epi_prefetch(EpiPre& ep, const ProjParams& pp, c
 // is written (for Q/K/V normalised) from the other into the buffer step s-1
 // read, while the MFMAs of step s read the other buffer.  The epilogue's own
 // loads go out before the last two steps.
-template <int MODE, bool TR>
+// BUSY = false: the wave's rows all lie past M (the upper half of a 64-row
+// last tile); it still loads and stores its share of the tiles and meets
+// every barrier, but reads no fragments and issues no MFMAs.
+template <int MODE, bool TR, bool BUSY = true>
 __device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], EpiPre& ep, const ProjParams& pp,
                                           bf16* lds0, bf16* lds1, int m0, int n0, int tid,
                                           int wave, const EpiCtx& ec) {
@@ -603,15 +606,17 @@ __device__ __forceinline__ void gemm_main(f32x16 (&acc)[2][2], EpiPre& ep, const
     // u's MFMAs.
     constexpr bool kAhead = MODE == kOut;
     Frags f[2];
-    if (kAhead) read_frags<MODE>(f[0], rd, rd + GM * GP, wm, wn, half, col, 0);
+    if (BUSY && kAhead) read_frags<MODE>(f[0], rd, rd + GM * GP, wm, wn, half, col, 0);
 #pragma unroll
     for (int u = 0; u < GK / 16; ++u) {
-      if (kAhead) {
-        if (u + 1 < GK / 16) read_frags<MODE>(f[(u + 1) & 1], rd, rd + GM * GP, wm, wn, half, col, u + 1);
-      } else {
-        read_frags<MODE>(f[u & 1], rd, rd + GM * GP, wm, wn, half, col, u);
+      if constexpr (BUSY) {
+        if (kAhead) {
+          if (u + 1 < GK / 16) read_frags<MODE>(f[(u + 1) & 1], rd, rd + GM * GP, wm, wn, half, col, u + 1);
+        } else {
+          read_frags<MODE>(f[u & 1], rd, rd + GM * GP, wm, wn, half, col, u);
+        }
+        mfma_sub<TR>(acc, f[u & 1]);
       }
-      mfma_sub<TR>(acc, f[u & 1]);
       if (more) store_part<MODE>(wr, wr + GM * GP, nxt, tid, u);
     }
   };
@@ -939,14 +944,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(ProjParams pp, int mt
   ProjParams pe;
   EpiCtx ee;
   if (tr) {
-    gemm_main<MODE, true>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
+    if (valid)
+      gemm_main<MODE, true>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
+    else
+      gemm_main<MODE, true, false>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
     epilogue_inputs(pe, ee);
     __syncthreads();  // every wave is done reading the operand tiles
     if (valid) epi_stage<MODE, true, QKO>(acc, ep, pe, stg, ee);
     __syncthreads();
     if (valid) epi_store<MODE, true>(ep, pe, stg, ee);
   } else {
-    gemm_main<MODE, false>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
+    if (valid)
+      gemm_main<MODE, false>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
+    else
+      gemm_main<MODE, false, false>(acc, ep, pp, lds0, lds1, m0, n0, tid, wave, ec);
     epilogue_inputs(pe, ee);
     __syncthreads();
     if (valid) epi_stage<MODE, false, QKO>(acc, ep, pe, stg, ee);
