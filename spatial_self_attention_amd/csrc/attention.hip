@@ -368,6 +368,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (REL != 0 ? 2 : attn_min_blocks<
     rp.tab = static_cast<const bf16*>(ap.rel) + head;
     rp.H = ap.H;
     rp.W = ap.W;
+    rp.w4 = ap.W % 4 == 0;
     rp.n = ap.n;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {  // rows past T take the last query's place
@@ -795,6 +796,7 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
     rp.tab = static_cast<const bf16*>(ap.rel) + head;
     rp.H = ap.H;
     rp.W = ap.W;
+    rp.w4 = ap.W % 4 == 0;
     rp.n = ap.n;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {  // rows past T take the last query's place

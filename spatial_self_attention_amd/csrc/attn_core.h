@@ -133,6 +133,7 @@ struct RelPos {
   int qrow[QB];        // REL = 2: (row(q) + H - 1)(2W - 1) + col(q) + W - 1 - lo
   const int* kterm;    // REL = 2: row(k)(2W - 1) + col(k) of the tile's keys (LDS)
   int k0;              // REL = 2: the tile's first key
+  bool w4;             // REL = 2: W % 4 == 0 (4-aligned runs of keys stay in one grid row)
 };
 
 // Entries of the table slice one work-group stages per key tile (REL = 2),
@@ -159,17 +160,35 @@ template <int QB, int REL>
 __device__ __forceinline__ void add_rel(f32x16 (&s)[QB], const RelPos<QB>& rp, int kfirst, int T,
                                         int half) {
   if constexpr (REL == 2) {
-    // table row of (q, k) = qrow(q) + lo - kterm(k): a run's four key terms
-    // come in one 16-byte LDS read, each score's entry in one more
+    // table row of (q, k) = qrow(q) + lo - kterm(k).  With W % 4 == 0 a run
+    // of four keys (4-aligned) lies in one grid row, so their terms are
+    // kterm(k0) + 0..3 and the entries are four consecutive slice entries
+    // below one base: one address and two paired LDS reads per run and query
+    // block.  Otherwise a run's four key terms come in one 16-byte LDS read,
+    // each score's entry in one more.
+    if (rp.w4) {
 #pragma unroll
-    for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
-      const int kk = kfirst - rp.k0 + 8 * run + 4 * half;
-      const int4 kt = *reinterpret_cast<const int4*>(rp.kterm + kk);
-      const int kte[4] = {kt.x, kt.y, kt.z, kt.w};
+      for (int run = 0; run < 4; ++run) {
+        const int kk = kfirst - rp.k0 + 8 * run + 4 * half;
+        const int kt0 = rp.kterm[kk];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb) {
+          const float* b = rp.slice + (rp.qrow[qb] - kt0 - 3);  // entries of keys 3, 2, 1, 0
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[qb][4 * run + e] += rp.slice[rp.qrow[qb] - kte[e]];
+          for (int e = 0; e < 4; ++e) s[qb][4 * run + e] += b[3 - e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int run = 0; run < 4; ++run) {  // keys kfirst + 8 run + 4 half + e, e = 0..3
+        const int kk = kfirst - rp.k0 + 8 * run + 4 * half;
+        const int4 kt = *reinterpret_cast<const int4*>(rp.kterm + kk);
+        const int kte[4] = {kt.x, kt.y, kt.z, kt.w};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[qb][4 * run + e] += rp.slice[rp.qrow[qb] - kte[e]];
+      }
     }
   } else {
 #pragma unroll
