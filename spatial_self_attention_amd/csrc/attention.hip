@@ -33,6 +33,17 @@
 // one v_add (the row sum).  m is raised lazily, only when a lane's 16 probabilities of a
 // sub-block sum past 2^8; then O and l are rescaled and that sub-block redone.
 //
+// Long sequences at d = 64 take kernels with two 32-query blocks per wave
+// (each K and V^T fragment read feeds two MFMAs): attn2_bf16_kernel (512- or
+// 256-query work-groups) and attnpp_bf16_kernel (one 8-wave work-group per
+// 256-query tile, two 4-wave groups walking the two halves of the keys in
+// alternating half steps -- one wave of each SIMD issues MFMAs while the other
+// runs its softmax -- merged in LDS at the end).  When the tiles of a last,
+// partial round fill at most half the CUs, each of them is cut into key ranges
+// run as separate work-groups, whose partial (O, m, l) attn_merge_kernel
+// combines.  The relative-position bias (REL) is staged per key tile as a
+// slice of the head's table column in LDS.
+//
 // fp32 kernel: 64 queries x 4 lanes per query (each lane owns d/4 dims),
 // FMA only, key tiles of 32 in LDS.
 #include <math.h>
