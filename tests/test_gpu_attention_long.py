@@ -79,6 +79,10 @@ CASES = [
                               # 64 each cut into 4 key ranges
     (2, 9, 64, 64, 40),       # 288 tiles: the last 32 in 8 key ranges of 2 tile pairs
     (1, 17, 66, 64, 40),      # 289 tiles, T % 256 = 128: the last 33 in 7 uneven key ranges
+    (1, 89, 32, 32, 24),      # 356 tiles: the last 100 in 2 key ranges
+    (1, 81, 32, 32, 24),      # 324 tiles: the last 68 in 3
+    (1, 75, 32, 32, 24),      # 300 tiles: the last 44 in 5
+    (1, 74, 32, 32, 24),      # 296 tiles: the last 40 in 6
     (1, 5, 32, 32, None),     # 20 tiles: one-block kernel
     (1, 32, 63, 63, 40),      # 256 query tiles of 512: T % 128 = 1, last tile 385 rows
     (2, 16, 64, 64, 48),      # 256 query tiles of 512, even sizes
