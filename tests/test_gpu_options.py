@@ -165,15 +165,17 @@ def test_relpos_wide_image(flags, stress):
     assert e <= TOL[wl.dtype]
 
 
-# Every option on (the relative-position bias keeps the one-block attention
-# kernel), and query/key normalisation with rotary embeddings at the
-# high-resolution workload, where the two-query-block attention kernel runs;
-# plain and stressed draws.
+# The workloads at full size with options: every option on at workloads 1
+# and 2 (one-block attention kernel with the bias), 3 (the key-splitting
+# kernel with the bias, its last round cut into key ranges) and 4, and the
+# options one or two at a time at workload 4; plain and stressed draws.
 @pytest.mark.parametrize("stress", [False, True], ids=["plain", "stressed"])
-@pytest.mark.parametrize("idx,rel,rope,qkn", [(1, True, True, True), (3, True, True, True),
+@pytest.mark.parametrize("idx,rel,rope,qkn", [(1, True, True, True), (2, True, True, True),
+                                              (3, True, True, True),
                                               (4, False, True, True), (4, False, True, False),
                                               (4, True, False, False), (4, True, True, True)],
-                         ids=["1-all", "3-all", "4-qknorm-rope", "4-rope", "4-relpos", "4-all"])
+                         ids=["1-all", "2-all", "3-all", "4-qknorm-rope", "4-rope", "4-relpos",
+                              "4-all"])
 def test_options_full_size_sampled(idx, rel, rope, qkn, stress):
     wl = WORKLOADS[idx]
     x, p, opts, out = run_case(wl, 1000 + idx, stress, drop_bias=("k_bias",),
