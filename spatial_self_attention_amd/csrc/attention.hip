@@ -770,10 +770,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn2_bf16_kernel(AttnParams ap
 // alternates two kinds of half step over its 32-key sub-blocks j:
 //   M_j  the MFMAs: scores S_j = K_j Q^T - m of both query blocks (8), then
 //        O^T += V_{j-1}^T P_{j-1}^T of both (8);
-//   V_j  the softmax of S_j on the VALU, both query blocks at once (bf16
-//        probabilities P_j, row sums, the lazy raise of m), at raised issue
-//        priority, and the LDS reads of V_j's fragments (M_{j+1} reads
-//        K_{j+1}'s before its P V products).
+//   V_j  the softmax of S_j on the VALU (bf16 probabilities P_j, row sums,
+//        the lazy raise of m; without the bias both query blocks at once, at
+//        raised issue priority) and the LDS reads of V_j's fragments (M_{j+1}
+//        reads K_{j+1}'s before its P V products).
 // The groups run half a step apart and every half step ends at a barrier of
 // all 8 waves, so on each SIMD one wave's MFMAs run while the other wave's
 // softmax runs: the matrix core and the VALU work side by side instead of
@@ -942,19 +942,30 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
       qk_qb<D>(s[1], st, 1, kf);
     }
   };
-  // V half step: softmax of S_j, both blocks at once; V_j's fragments (needed
-  // first by the next M's P V products) are requested before it.  The wave
-  // raises its issue priority for the step: the exponentials bound the step,
-  // and the MFMA wave beside it on the SIMD needs few issue slots (measured:
-  // 2-3% faster than the default priority).
+  // V half step: softmax of S_j; V_j's fragments are needed first by the next
+  // M's P V products.  Without the bias: both blocks at once, the fragments
+  // requested before it, at raised issue priority (the exponentials bound the
+  // step, and the MFMA wave beside it on the SIMD needs few issue slots;
+  // measured: 2-3% faster than block by block at the default priority).
   auto v_step = [&](const bf16* cur, int u, int kb, bool first) {
     rel_add(u, kb);
-    __builtin_amdgcn_s_setprio(1);
-    read_v<D, 2, KT>(vf, cur + TL::KSZ, kb, half, col);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax_pair<D>(st, s, pb, first);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (REL == 0) {
+      __builtin_amdgcn_s_setprio(1);
+      read_v<D, 2, KT>(vf, cur + TL::KSZ, kb, half, col);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_pair<D>(st, s, pb, first);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      // with the bias the step is longer and the V^T reads are better placed
+      // between the blocks, block by block at default priority (measured: the
+      // paired form 3-4% slower here)
+      softmax_qb<D, 2, false>(st, 0, s[0], pb[0], 0, T, half, first);
+      __builtin_amdgcn_sched_barrier(0);
+      read_v<D, 2, KT>(vf, cur + TL::KSZ, kb, half, col);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_qb<D, 2, false>(st, 1, s[1], pb[1], 0, T, half, first);
+    }
   };
   auto request = [&](int u) {  // tile u of the group into buffer u % 3 (slice first)
     rel_load(u);
