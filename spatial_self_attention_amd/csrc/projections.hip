@@ -53,6 +53,9 @@ struct ProjParams {
   int rope;            // rotary embedding on
   const float2* rope_tab;  // (T, d/2) (cos, sin) of the rotary angles
   float* qk32;         // (2, B, n, T, d) fp32 Q and K for the separate option pass, or NULL
+  int nt_out;          // kOut: T % 64 == 0, so a wave's 64-token run of an output channel row
+                       // is whole 128-byte lines (stored non-temporally); otherwise the runs
+                       // straddle lines, whose pieces L2 joins (cached stores)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -866,7 +869,10 @@ __device__ __forceinline__ void epi_store(const EpiPre& ep, const ProjParams& pp
         bf16x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk[e] = static_cast<bf16>(xv[e] + y[e]);
-        store_nt(out + idx, pk);
+        if (pp.nt_out)
+          store_nt(out + idx, pk);
+        else
+          *reinterpret_cast<bf16x4*>(out + idx) = pk;
       }
     } else {
       const bf16* E = stg;
@@ -1076,6 +1082,7 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjParams pp) {
 ProjParams make_params(const Plan& p, const Args& a, int mode) {
   ProjParams pp{};
   pp.x = a.x;
+  pp.nt_out = p.T % 64 == 0;
   if (mode == kQkv) {
     for (int i = 0; i < 3; ++i) {
       pp.w[i] = a.w[i];
