@@ -927,10 +927,12 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   KFrag<D> kf;
   VFrag<D> vf;
   bf16x8 pb[2][2];
-  // M half step on sub-block kb of the tile in `cur`: K_j's fragments are
-  // read first (their LDS latency hides behind the P V products, and they are
-  // not live during the softmax), then O^T += V_{j-1}^T P_{j-1}^T, then
-  // S_j = K_j Q^T - m.
+  // M half step on sub-block kb of the tile in `cur`: K_j's fragment reads,
+  // O^T += V_{j-1}^T P_{j-1}^T, then S_j = K_j Q^T - m.  (The compiler issues
+  // the reads after the P V products, into the registers their V operands
+  // free, so the score MFMAs wait on the LDS latency; issuing them first, in
+  // registers of their own, measured slower: MFMAs issued earlier take issue
+  // slots from the other wave's softmax.)
   auto m_step = [&](const bf16* cur, int u, int kb, bool pv, bool qk) {
     if (qk) read_k<D, 2, KT>(kf, cur, kb, half, col);
     if (pv) {
