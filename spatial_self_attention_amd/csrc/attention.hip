@@ -933,7 +933,7 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   // free, so the score MFMAs wait on the LDS latency; issuing them first, in
   // registers of their own, measured slower: MFMAs issued earlier take issue
   // slots from the other wave's softmax.)
-  auto m_step = [&](const bf16* cur, int u, int kb, bool pv, bool qk) {
+  auto m_step = [&](const bf16* cur, int kb, bool pv, bool qk) {
     if (qk) read_k<D, 2, KT>(kf, cur, kb, half, col);
     if (pv) {
       pv_qb<D, 2>(st, 0, pb[0], vf);
@@ -976,11 +976,11 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
 
   if (grp == 1) phase_barrier();  // group 1 runs half a step behind
   // tile 0: its first sub-block starts the running max
-  m_step(mine, 0, 0, false, true);
+  m_step(mine, 0, false, true);
   phase_barrier();
   v_step(mine, 0, 0, true);
   phase_barrier();  // (tile 1 arrived before the first barrier)
-  m_step(mine, 0, 1, true, true);
+  m_step(mine, 1, true, true);
   if (2 < nh) request(2);
   phase_barrier();
   v_step(mine, 0, 1, false);
@@ -988,20 +988,20 @@ __global__ __launch_bounds__(512, 1) void attnpp_bf16_kernel(AttnParams ap) {
   int bu = 1;  // buffer of tile u
   for (int u = 1; u < nh; ++u) {
     const bf16* cur = mine + bu * TL::BUF;
-    m_step(cur, u, 0, true, true);
+    m_step(cur, 0, true, true);
     if (u + 1 < nh) rel_store(u + 1);  // requested in the M half step before
     phase_barrier();
     v_step(cur, u, 0, false);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile u + 1 is in
     phase_barrier();
-    m_step(cur, u, 1, true, true);
+    m_step(cur, 1, true, true);
     if (u + 2 < nh) request(u + 2);    // into the buffer of tile u - 1
     phase_barrier();
     v_step(cur, u, 1, false);
     phase_barrier();
     bu = bu + 1 == NBUF ? 0 : bu + 1;
   }
-  m_step(mine, 0, 0, true, false);  // the last sub-block's P V
+  m_step(mine, 0, true, false);  // the last sub-block's P V
   phase_barrier();
   if (grp == 0) phase_barrier();  // both groups pass the same number of barriers
 
