@@ -8,7 +8,7 @@ the tiles of a partial last round cut into 4, 7 or 8 key ranges whose
 partial results a second kernel merges (one round of tiles and a last round
 filling at most half the CUs), and the one-block kernel when the query
 tiles are too few to fill whole rounds of the CUs (the choice assumes
-MI355X's 256 CUs).
+MI355X's 256 CUs); and six seeded random shapes for the key-splitting kernel.
 
 Seeded Q, K, V (spatial_self_attention_amd.inputs.draw_qkv) are written into
 the workspace in the layouts the stage reads, the stage runs alone, and O is
@@ -94,9 +94,26 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("kind", ["peaked", "ramp"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}-n{c[1]}-{c[2]}x{c[3]}")
-def test_attention_stage_long(case, kind):
+def _random_cases(n_cases=6, seed=20261202):
+    """Seeded shapes nobody chose for the key-splitting kernel: T = 128 m in
+    [1024, 8192] as an H x W grid, at least one round of 256-query tiles on
+    256 CUs (some with the last round cut into key ranges)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n_cases:
+        T = 128 * int(rng.integers(8, 65))
+        widths = [w for w in range(8, 257) if T % w == 0 and T // w >= 4]
+        W = int(rng.choice(widths))
+        B, n = int(rng.integers(1, 4)), int(rng.integers(1, 31))
+        if B * n * ((T + 255) // 256) >= 256:
+            out.append((B, n, T // W, W, 16))
+    return out
+
+
+RANDOM_CASES = _random_cases()
+
+
+def check_long(case, kind):
     B, n, H, W, per_head = case
     T = H * W
     q, k, v, o = run_attention(B, n, H, W, 40 + n + H, kind)
@@ -116,3 +133,14 @@ def test_attention_stage_long(case, kind):
         worst = max(worst, e)
     print(f"  err {worst:.3e}", flush=True)
     assert worst <= TOL
+
+
+@pytest.mark.parametrize("kind", ["peaked", "ramp"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}-n{c[1]}-{c[2]}x{c[3]}")
+def test_attention_stage_long(case, kind):
+    check_long(case, kind)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: f"B{c[0]}-n{c[1]}-{c[2]}x{c[3]}")
+def test_attention_stage_long_random(case):
+    check_long(case, "ramp" if case[1] % 2 else "peaked")
