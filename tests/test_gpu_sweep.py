@@ -4,8 +4,12 @@ The other parity tests pick their shapes by hand; this one draws 40 from a
 fixed seed so that sizes nobody chose get checked too: both dtypes, every
 supported bf16 head size, odd image sizes (ragged token tiles, grid rows not a
 multiple of any tile), group counts that do not divide the heads, the optional
-steps in random combinations and absent biases.  The list is fixed (seeded),
-so a failure names a reproducible case.  Tolerances as in test_gpu_parity.
+steps in random combinations and absent biases.  A second seeded list of
+medium bf16 shapes (channels a multiple of 64, up to 4096 pixels, up to 32
+heads) takes the tiled projection GEMMs and the larger attention kernels,
+checked on sampled pixels of the first and last sample.  The lists are fixed
+(seeded), so a failure names a reproducible case.  Tolerances as in
+test_gpu_parity.
 """
 import numpy as np
 import pytest
@@ -68,3 +72,52 @@ def test_random_shape(wl, flags, drop):
         e /= max(float(np.max(np.abs(want))), 1e-30)
     print(f"  err {e:.3e}", flush=True)
     assert e <= TOL[wl.dtype]
+
+
+def _medium_cases(n_cases=8, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n_cases):
+        d = int(rng.choice([32, 64, 96, 128]))
+        n = int(rng.integers(1, 33))
+        while (n * d) % 64 or n * d > 1024:
+            n = int(rng.integers(1, 33))
+        C = n * d
+        G = int(rng.choice([g for g in (1, 2, 4, 8, 16, 32) if C % g == 0]))
+        H, W = int(rng.integers(8, 65)), int(rng.integers(8, 65))
+        while (H * W) % 4:  # the tiled projection path takes whole runs of 4 pixels
+            W += 1
+        B = int(rng.integers(1, 5))
+        flags = dict(rel_pos=bool(rng.random() < 0.25), qk_norm=bool(rng.random() < 0.25),
+                     rope=bool(rng.random() < 0.25))
+        out.append((Workload(f"medium{i}", "bf16", B, C, H, W, G, n), flags))
+    return out
+
+
+MEDIUM_CASES = _medium_cases()
+
+
+@pytest.mark.parametrize("wl,flags", MEDIUM_CASES, ids=[c[0].name for c in MEDIUM_CASES])
+def test_random_medium_shape(wl, flags):
+    x, p = draw(wl, 310)
+    opts = draw_options(wl, 310, **flags)
+    print(f"[gpu] {wl.name} B={wl.B} C={wl.C} H={wl.H} W={wl.W} G={wl.num_groups} "
+          f"n={wl.num_heads} opts={flags}", flush=True)
+    dev = lambda t: None if t is None else t.to(DEV)
+    out = ssa.spatial_self_attention(
+        x.to(DEV), {k: dev(v) for k, v in p.items()}, wl.num_groups, wl.num_heads,
+        rel_pos_table=dev(opts["rel_pos_table"]), q_norm_gamma=dev(opts["q_norm_gamma"]),
+        k_norm_gamma=dev(opts["k_norm_gamma"]), rope=opts["rope"])
+    torch.cuda.synchronize()
+    og = out.double().cpu().numpy().reshape(wl.B, wl.C, wl.T)
+    assert np.isfinite(og).all()
+    x64, p64 = to_f64(x, p)
+    rng = np.random.default_rng(wl.T)
+    worst = 0.0
+    for b in sorted({0, wl.B - 1}):
+        rows = np.unique(np.concatenate([[0, wl.T - 1], rng.integers(0, wl.T, 8)]))
+        want = ORA.forward_pixels(x64, p64, wl.num_groups, wl.num_heads, b, rows, **options_f64(opts))
+        e = float(np.max(np.abs(og[b][:, rows] - want))) / float(np.max(np.abs(want)))
+        worst = max(worst, e)
+    print(f"  sampled err {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
